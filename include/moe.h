@@ -1,0 +1,142 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) token-choice top-k mixture-of-experts
+ * feed-forward layer, forward pass.
+ *
+ * What the layer computes (per token t of x, D features):
+ *   logits[t,e] = x[t] . router[e] (+ router_bias[e])            e < E
+ *   p[t]        = softmax over the E logits
+ *   sel[t,0..K) = the K largest p[t,e] in descending order, equal values to
+ *                 the lower expert index
+ *   w[t,k]      = p[t,sel] / (sum_k p[t,sel] + 1e-9) if norm_topk, else p[t,sel]
+ *   y_e(x)      = SwiGLU: down_proj[e] (silu(gate) * up), gate = rows [0,F) of
+ *                 gate_up_proj[e] times x, up = rows [F,2F);
+ *                 ReLU:   W2[e] relu(W1[e] x + b1[e]) + b2[e]
+ *   out[t]      = sum_k w[t,k] * y_{sel[t,k]}(x[t])
+ * Sources: the mojolearn "MoEBlock" API page (class description, "Variables",
+ * "Parameters"), the crackedaicode "Mixture-of-Experts FFN" exercise (sections
+ * "Compute the experts and router" and "Weight the selected outputs"), and the
+ * Dew "Mixture of experts" page, section "Expert computation and placement"
+ * (tokens are sorted into expert order and the experts run as one grouped
+ * matrix product; each contraction accumulates in at least fp32 and rounds once
+ * to the compute dtype).
+ *
+ * Conventions for every entry point
+ *   - Tensors are contiguous, row-major DEVICE pointers unless stated.  Weights
+ *     use the Hugging Face layouts: router (E,D), gate_up_proj (E,G*F,D) with
+ *     G=2 for SwiGLU (W1 (E,F,D) with G=1 for ReLU), down_proj (E,D,F).
+ *   - The caller owns every buffer.  The library never writes its inputs,
+ *     allocates no device memory and keeps no state; scratch memory is the
+ *     caller's workspace, sized by moe_workspace_bytes.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream).  No entry point synchronises with the host.
+ *   - Arguments are validated on the host before anything is enqueued.  On an
+ *     error nothing is written and nothing is launched.  MOE_EDEVICE means a
+ *     launch failed; outputs are then undefined.
+ *   - T = 0 is valid: MOE_OK and no work.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,     /* a size out of range (K not in [1,E], D/F/E <= 0, T < 0,
+                         sizes over the library limits) or a NULL required pointer */
+  MOE_ENOTSUP = 2,    /* activation other than SwiGLU / ReLU */
+  MOE_ETYPE = 3,      /* dtype other than fp32 / bf16 */
+  MOE_EWORKSPACE = 4, /* workspace smaller than moe_workspace_bytes */
+  MOE_EDEVICE = 5     /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU = 1 } moe_act;
+
+/* Shape and mode of one layer call. */
+typedef struct {
+  int64_t T;             /* tokens (rows of x), >= 0                        */
+  int64_t D;             /* model width, >= 1                               */
+  int64_t F;             /* expert hidden width, >= 1                       */
+  int32_t E;             /* experts, 1..MOE_MAX_EXPERTS                     */
+  int32_t K;             /* experts per token, 1..E                         */
+  int32_t norm_topk;     /* 1: renormalise the kept probabilities           */
+  int32_t act;           /* moe_act                                         */
+  int32_t dtype;         /* moe_dtype of x, router, gate_up_proj, down_proj */
+  int32_t out_dtype;     /* moe_dtype of out                                */
+  int32_t deterministic; /* 1: out[t] sums its K expert outputs in k order,
+                            bitwise reproducible for any K; 0: the down
+                            projection adds into out with fp32 atomics
+                            (reproducible for K <= 2 only)                 */
+} moe_desc;
+
+#define MOE_MAX_EXPERTS 256
+
+/*
+ * moe_workspace_bytes -- device scratch needed by moe_forward / moe_dispatch
+ * for *d.  Writes the size to *bytes.  MOE_EINVAL / MOE_ETYPE / MOE_ENOTSUP as
+ * for moe_forward.  Host-only; touches no device.
+ */
+moe_status moe_workspace_bytes(const moe_desc* d, size_t* bytes);
+
+/*
+ * moe_forward -- the whole layer forward.
+ *   x            (T,D)       dtype
+ *   router       (E,D)       dtype
+ *   gate_up_proj (E,G*F,D)   dtype  (SwiGLU: gate rows [0,F), up rows [F,2F))
+ *   down_proj    (E,D,F)     dtype
+ *   router_bias  (E)         fp32 or NULL
+ *   up_bias      (E,G*F)     fp32 or NULL  (added before the activation)
+ *   down_bias    (E,D)       fp32 or NULL  (added to the expert output before
+ *                                            it is weighted)
+ * Outputs:
+ *   out              (T,D)   out_dtype (fp32 recommended for bf16 inputs)
+ *   selected_experts (T,K)   int64, descending probability
+ *   routing_weights  (T,K)   fp32
+ *   router_logits    (T,E)   fp32, or NULL
+ *   expert_counts    (E)     int32 tokens routed to each expert, or NULL
+ * Precision: router logits and softmax in fp32; expert contractions with
+ * fp32 accumulation; for bf16 the gate/up accumulators stay fp32 and the
+ * activation output is rounded once to bf16 before the down projection.
+ */
+moe_status moe_forward(const moe_desc* d, const void* x, const void* router, const void* gate_up_proj,
+                       const void* down_proj, const float* router_bias, const float* up_bias,
+                       const float* down_bias, void* out, int64_t* selected_experts, float* routing_weights,
+                       float* router_logits, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * moe_dispatch -- the router and the sort into expert order alone (the
+ * "global" dispatch of the Dew page: tokens sorted into expert order so each
+ * expert's rows are contiguous).  The order is stable: inside an expert's
+ * segment, assignments appear in increasing (t, k).
+ *   selected_experts (T,K) int64, routing_weights (T,K) fp32,
+ *   router_logits (T,E) fp32 or NULL,
+ *   expert_counts (E) int32, expert_offsets (E+1) int32 (exclusive scan of
+ *   the counts, expert_offsets[E] = T*K),
+ *   sorted_token (T*K) int32: token of the r-th row of the sorted order,
+ *   sorted_slot  (T*K) int32: t*K + k of that row.
+ * Uses the same workspace as moe_forward (moe_workspace_bytes of d).
+ */
+moe_status moe_dispatch(const moe_desc* d, const void* x, const void* router, const float* router_bias,
+                        int64_t* selected_experts, float* routing_weights, float* router_logits,
+                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_token,
+                        int32_t* sorted_slot, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* moe_status_string(moe_status s);
+
+/* ABI version of this header (bumped on any signature change). */
+int32_t moe_abi_version(void);
+#define MOE_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,242 @@
+"""MI355X-native forward pass of a token-choice top-k mixture-of-experts
+feed-forward layer.
+
+The layer runs in ``libmoe.so`` (hand-written HIP kernels for gfx950, C ABI in
+``include/moe.h``).  This module is a thin ctypes binding: the functions named
+like the C entry points (``moe_forward``, ``moe_dispatch``,
+``moe_workspace_bytes``, ``moe_status_string``, ``moe_abi_version``) marshal
+arguments and nothing else; ``forward`` additionally allocates the outputs and
+the workspace with PyTorch, on the device of ``x``, and returns them.  PyTorch
+provides device memory and the current stream; every step of the layer runs in
+the library's kernels.  There is no fallback: without the built library on a
+ROCm device every call raises.
+
+Semantics follow the mojolearn ``MoEBlock`` page (Hugging Face weight layouts
+router (E,D), gate_up_proj (E,2F,D), down_proj (E,D,F); output with the shape
+of x; selected experts int64 in descending probability; ValueError for a bad
+top_k or mismatched shapes, NotImplementedError for another activation,
+TypeError for float64) and the ReLU-expert exercise of the crackedaicode
+"Mixture-of-Experts FFN" page (biases, 1e-9-guarded renormalisation).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_ETYPE, MOE_EWORKSPACE, MOE_EDEVICE = range(6)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_ACT_SWIGLU, MOE_ACT_RELU = 0, 1
+MOE_MAX_EXPERTS = 256
+
+_ACTS = {"silu": MOE_ACT_SWIGLU, "swiglu": MOE_ACT_SWIGLU, "relu": MOE_ACT_RELU}
+
+
+class MoeDesc(ctypes.Structure):
+    """Mirror of ``moe_desc`` in include/moe.h."""
+    _fields_ = [("T", ctypes.c_int64), ("D", ctypes.c_int64), ("F", ctypes.c_int64),
+                ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("norm_topk", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("deterministic", ctypes.c_int32)]
+
+
+class MoEError(RuntimeError):
+    """A HIP launch or runtime failure reported by the library."""
+
+
+_lib = None
+
+
+def load_library():
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmoe.so is not built: run `python -m sparse_mixture_experts_02_amd.build` "
+                               "(the layer has no non-HIP fallback)")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, S, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+        D = ctypes.POINTER(MoeDesc)
+        lib.moe_workspace_bytes.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+        lib.moe_workspace_bytes.restype = ctypes.c_int
+        lib.moe_forward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+        lib.moe_forward.restype = ctypes.c_int
+        lib.moe_dispatch.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
+        lib.moe_dispatch.restype = ctypes.c_int
+        lib.moe_status_string.argtypes = [ctypes.c_int]
+        lib.moe_status_string.restype = ctypes.c_char_p
+        lib.moe_abi_version.argtypes = []
+        lib.moe_abi_version.restype = I32
+        _lib = lib
+    return _lib
+
+
+# ------------------------------------------------ entry points (C names)
+def moe_status_string(status: int) -> str:
+    return load_library().moe_status_string(int(status)).decode()
+
+
+def moe_abi_version() -> int:
+    return int(load_library().moe_abi_version())
+
+
+def moe_workspace_bytes(desc: MoeDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().moe_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def moe_forward(desc, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out,
+                selected_experts, routing_weights, router_logits, expert_counts, workspace, workspace_bytes,
+                stream) -> int:
+    """Raw call: pointers are integers (or None); returns the status code."""
+    return load_library().moe_forward(ctypes.byref(desc), x, router, gate_up_proj, down_proj, router_bias, up_bias,
+                                      down_bias, out, selected_experts, routing_weights, router_logits,
+                                      expert_counts, workspace, workspace_bytes, stream)
+
+
+def moe_dispatch(desc, x, router, router_bias, selected_experts, routing_weights, router_logits, expert_counts,
+                 expert_offsets, sorted_token, sorted_slot, workspace, workspace_bytes, stream) -> int:
+    """Raw call: pointers are integers (or None); returns the status code."""
+    return load_library().moe_dispatch(ctypes.byref(desc), x, router, router_bias, selected_experts,
+                                       routing_weights, router_logits, expert_counts, expert_offsets, sorted_token,
+                                       sorted_slot, workspace, workspace_bytes, stream)
+
+
+def _check(status: int) -> None:
+    if status == MOE_OK:
+        return
+    msg = moe_status_string(status)
+    if status in (MOE_EINVAL, MOE_EWORKSPACE):
+        raise ValueError(msg)
+    if status == MOE_ENOTSUP:
+        raise NotImplementedError(msg)
+    if status == MOE_ETYPE:
+        raise TypeError(msg)
+    raise MoEError(msg)
+
+
+# ------------------------------------------------------ torch marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    return {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}.get(t, -1)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def make_desc(T, D, F, E, K, *, norm_topk_prob=True, act="silu", dtype=None, out_dtype=None,
+              deterministic=False) -> MoeDesc:
+    return MoeDesc(T=int(T), D=int(D), F=int(F), E=int(E), K=int(K), norm_topk=int(bool(norm_topk_prob)),
+                   act=_ACTS.get(act, -1) if isinstance(act, str) else int(act),
+                   dtype=_dtype_code(dtype) if dtype is not None else MOE_F32,
+                   out_dtype=_dtype_code(out_dtype) if out_dtype is not None else MOE_F32,
+                   deterministic=int(bool(deterministic)))
+
+
+def _prepare(x, router, gate_up_proj, down_proj, top_k, act):
+    torch = _torch()
+    if x.dtype == torch.float64:
+        raise TypeError("float64 input is not supported")
+    D = x.shape[-1]
+    E = router.shape[0]
+    if router.dim() != 2 or router.shape[1] != D:
+        raise ValueError("router must be (E, D) = (%d, %d), got %s" % (E, D, tuple(router.shape)))
+    if down_proj.dim() != 3 or down_proj.shape[0] != E or down_proj.shape[1] != D:
+        raise ValueError("down_proj must be (E, D, F), got %s" % (tuple(down_proj.shape),))
+    F = down_proj.shape[2]
+    G = 1 if act == "relu" else 2
+    if gate_up_proj.shape != (E, G * F, D):
+        raise ValueError("gate_up_proj must be %s, got %s" % ((E, G * F, D), tuple(gate_up_proj.shape)))
+    for t in (router, gate_up_proj, down_proj):
+        if t.dtype != x.dtype:
+            raise TypeError("x and the weights must share one dtype")
+        if t.device != x.device:
+            raise ValueError("all tensors must be on one device")
+    if x.device.type != "cuda":
+        raise ValueError("tensors must live on a ROCm device")
+    return D, F, E
+
+
+def forward(x, router, gate_up_proj, down_proj, *, top_k, norm_topk_prob=True, act="silu", router_bias=None,
+            up_bias=None, down_bias=None, out_dtype=None, deterministic=False, return_logits=False,
+            return_counts=False, workspace=None):
+    """Layer forward on the device of x.
+
+    Returns (out with the shape of x, selected_experts int64 (T,K),
+    routing_weights fp32 (T,K)) plus router_logits (T,E) and expert_counts (E)
+    when requested.  ``out_dtype`` defaults to float32.
+    """
+    torch = _torch()
+    D, F, E = _prepare(x, router, gate_up_proj, down_proj, top_k, act)
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, D).contiguous()
+    T = x2.shape[0]
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    desc = make_desc(T, D, F, E, top_k, norm_topk_prob=norm_topk_prob, act=act, dtype=x.dtype,
+                     out_dtype=out_dtype, deterministic=deterministic)
+    nbytes = moe_workspace_bytes(desc)
+    dev = x.device
+    out = torch.empty((T, D), dtype=out_dtype, device=dev)
+    sel = torch.empty((T, top_k), dtype=torch.int64, device=dev)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if return_logits else None
+    counts = torch.empty((E,), dtype=torch.int32, device=dev) if return_counts else None
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    biases = [None if b is None else b.to(device=dev, dtype=torch.float32).contiguous()
+              for b in (router_bias, up_bias, down_bias)]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(moe_forward(desc, _ptr(x2), _ptr(router.contiguous()), _ptr(gate_up_proj.contiguous()),
+                       _ptr(down_proj.contiguous()), *(_ptr(b) for b in biases), _ptr(out), _ptr(sel), _ptr(w),
+                       _ptr(logits), _ptr(counts), _ptr(workspace), nbytes, stream))
+    res = [out.reshape(*lead, D), sel, w]
+    if return_logits:
+        res.append(logits)
+    if return_counts:
+        res.append(counts)
+    return tuple(res)
+
+
+def dispatch(x, router, *, top_k, norm_topk_prob=True, router_bias=None, num_experts=None, F=1):
+    """Router plus the stable sort into expert order.
+
+    Returns dict(selected_experts, routing_weights, router_logits,
+    expert_counts, expert_offsets, sorted_token, sorted_slot).
+    """
+    torch = _torch()
+    D = x.shape[-1]
+    E = router.shape[0] if num_experts is None else num_experts
+    x2 = x.reshape(-1, D).contiguous()
+    T = x2.shape[0]
+    desc = make_desc(T, D, F, E, top_k, norm_topk_prob=norm_topk_prob, dtype=x.dtype)
+    nbytes = moe_workspace_bytes(desc)
+    dev = x.device
+    M = T * top_k
+    r = dict(selected_experts=torch.empty((T, top_k), dtype=torch.int64, device=dev),
+             routing_weights=torch.empty((T, top_k), dtype=torch.float32, device=dev),
+             router_logits=torch.empty((T, E), dtype=torch.float32, device=dev),
+             expert_counts=torch.empty((E,), dtype=torch.int32, device=dev),
+             expert_offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
+             sorted_token=torch.empty((M,), dtype=torch.int32, device=dev),
+             sorted_slot=torch.empty((M,), dtype=torch.int32, device=dev))
+    ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    rb = None if router_bias is None else router_bias.to(device=dev, dtype=torch.float32).contiguous()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(moe_dispatch(desc, _ptr(x2), _ptr(router.contiguous()), _ptr(rb), _ptr(r["selected_experts"]),
+                        _ptr(r["routing_weights"]), _ptr(r["router_logits"]), _ptr(r["expert_counts"]),
+                        _ptr(r["expert_offsets"]), _ptr(r["sorted_token"]), _ptr(r["sorted_slot"]), _ptr(ws),
+                        nbytes, stream))
+    return r
+
+
+__all__ = ["MoeDesc", "MoEError", "load_library", "moe_forward", "moe_dispatch", "moe_workspace_bytes",
+           "moe_status_string", "moe_abi_version", "make_desc", "forward", "dispatch", "LIB_PATH"]

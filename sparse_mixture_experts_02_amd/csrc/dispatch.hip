@@ -1,0 +1,180 @@
+// Sort of the T*K (token, expert) assignments into expert-contiguous order
+// (the Dew "Mixture of experts" page, section "Expert computation and
+// placement": tokens are sorted into expert order so the experts run as one
+// grouped product).  A stable counting sort in three launches:
+//
+//   count   one block per chunk of 1024 assignments: LDS histogram per expert
+//   scan    one block: per-expert totals, the exclusive scan into segment
+//           offsets, each chunk's starting row inside every segment, and the
+//           tile table of the grouped GEMMs (empty experts get no tile, so
+//           they launch no MFMA work)
+//   scatter one block per chunk: the chunk is walked in order; inside a wave
+//           equal experts are found with nine ballots (expert id bits plus a
+//           validity bit) and ranked by popcount, and waves are ordered
+//           through per-wave counts in LDS.  Row order inside a segment is
+//           therefore increasing (t, k).
+//
+// The host never reads the counts: the GEMM grids are sized by the bound
+// ceil(T*K / bm) + E on the number of tiles and surplus blocks exit.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kScanThreads = 1024;
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void count_kernel(DispatchArgs a) {
+  __shared__ int hist[kMaxExperts];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < a.E; e += kThreads) hist[e] = 0;
+  __syncthreads();
+  const int64_t beg = (int64_t)blockIdx.x * kDispatchChunk;
+  const int64_t end = min(a.M, beg + kDispatchChunk);
+  for (int64_t i = beg + tid; i < end; i += kThreads) atomicAdd(&hist[a.sel32[i]], 1);
+  __syncthreads();
+  for (int e = tid; e < a.E; e += kThreads) a.chunk_counts[(int64_t)blockIdx.x * a.E + e] = hist[e];
+}
+
+// Exclusive scan of v[0..n) (n <= kScanThreads) in LDS; returns the total.
+__device__ int block_exclusive_scan(int* v, int* tmp, int n) {
+  const int tid = threadIdx.x;
+  int x = tid < n ? v[tid] : 0;
+  tmp[tid] = x;
+  __syncthreads();
+  for (int off = 1; off < n; off <<= 1) {
+    int y = (tid >= off && tid < n) ? tmp[tid - off] : 0;
+    __syncthreads();
+    if (tid < n) tmp[tid] += y;
+    __syncthreads();
+  }
+  const int total = n > 0 ? tmp[n - 1] : 0;
+  if (tid < n) v[tid] = tmp[tid] - x;
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(DispatchArgs a) {
+  __shared__ int part[kScanThreads];   // [J][E] partial chunk sums, then their prefixes
+  __shared__ int tmp[kScanThreads];
+  __shared__ int offs[kMaxExperts];
+  __shared__ int tstart[kMaxExperts];
+  __shared__ int cnts[kMaxExperts];
+  const int tid = threadIdx.x;
+  const int E = a.E;
+  const int J = kScanThreads / E;      // chunk-range lanes per expert
+  const int e = tid % E, j = tid / E;
+  const bool worker = j < J;
+  const int nch = a.nchunks;
+  const int cb = worker ? (int)((int64_t)j * nch / J) : 0;
+  const int ce = worker ? (int)((int64_t)(j + 1) * nch / J) : 0;
+
+  int s = 0;
+  for (int b = cb; b < ce; ++b) s += a.chunk_counts[(int64_t)b * E + e];
+  if (worker) part[j * E + e] = s;
+  __syncthreads();
+  if (tid < E) {
+    int run = 0;
+    for (int jj = 0; jj < J; ++jj) {
+      const int v = part[jj * E + tid];
+      part[jj * E + tid] = run;
+      run += v;
+    }
+    offs[tid] = run;                                    // count, scanned below
+    tstart[tid] = (run + a.bm - 1) / a.bm;              // tiles, scanned below
+    cnts[tid] = run;
+    a.counts[tid] = run;
+    if (a.counts_out) a.counts_out[tid] = run;
+  }
+  __syncthreads();
+  const int M = block_exclusive_scan(offs, tmp, E);
+  const int ntiles = block_exclusive_scan(tstart, tmp, E);
+  if (tid < E) {
+    a.offsets[tid] = offs[tid];
+    if (a.offsets_out) a.offsets_out[tid] = offs[tid];
+  }
+  if (tid == 0) {
+    a.offsets[E] = M;
+    if (a.offsets_out) a.offsets_out[E] = M;
+    a.num_tiles[0] = ntiles;
+  }
+  if (worker) {
+    int base = offs[e] + part[j * E + e];
+    for (int b = cb; b < ce; ++b) {
+      const int64_t idx = (int64_t)b * E + e;
+      const int c = a.chunk_counts[idx];
+      a.chunk_base[idx] = base;
+      base += c;
+    }
+    const int cnt = cnts[e];
+    const int nt = (cnt + a.bm - 1) / a.bm;
+    for (int t = j; t < nt; t += J) {
+      const int slot = tstart[e] + t;
+      if (slot < a.max_tiles) {
+        a.tile_e[slot] = e;
+        a.tile_r0[slot] = offs[e] + t * a.bm;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void scatter_kernel(DispatchArgs a) {
+  __shared__ int running[kMaxExperts];
+  __shared__ int wcount[kThreads / 64][kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int E = a.E;
+  for (int e = tid; e < E; e += kThreads) {
+    running[e] = a.chunk_base[(int64_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int q = 0; q < kThreads / 64; ++q) wcount[q][e] = 0;
+  }
+  __syncthreads();
+  const int64_t beg = (int64_t)blockIdx.x * kDispatchChunk;
+  const int64_t end = min(a.M, beg + kDispatchChunk);
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int64_t base = beg; base < end; base += kThreads) {
+    const int64_t i = base + tid;
+    const bool valid = i < end;
+    const int e = valid ? a.sel32[i] : kMaxExperts;   // the sentinel only matches itself
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int bit = 0; bit < 9; ++bit) {
+      const int on = (e >> bit) & 1;
+      const uint64_t b = __ballot(on);
+      same &= on ? b : ~b;
+    }
+    const int rank = __popcll(same & below);
+    if (valid && rank == 0) wcount[w][e] = __popcll(same);
+    __syncthreads();
+    if (valid) {
+      int pos = running[e] + rank;
+      for (int q = 0; q < w; ++q) pos += wcount[q][e];
+      a.sorted_tok[pos] = (int32_t)(i / a.K);
+      a.sorted_slot[pos] = (int32_t)i;
+      if (a.sorted_w) a.sorted_w[pos] = a.weights[i];
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += kThreads) {
+      int add = 0;
+#pragma unroll
+      for (int q = 0; q < kThreads / 64; ++q) {
+        add += wcount[q][x];
+        wcount[q][x] = 0;
+      }
+      running[x] += add;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(count_kernel, dim3(a.nchunks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
+  hipLaunchKernelGGL(scatter_kernel, dim3(a.nchunks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

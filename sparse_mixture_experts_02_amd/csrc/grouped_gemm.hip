@@ -1,0 +1,319 @@
+// Grouped expert GEMMs over the expert-sorted rows, with fused epilogues.
+//
+//   gate_up (SwiGLU): h[r, n] = silu(x_r . Wgu[e][n]) * (x_r . Wgu[e][F + n])
+//                     (gate = rows [0,F) of gate_up_proj[e], up = rows [F,2F);
+//                     mojolearn "MoEBlock" class description and "Variables")
+//   gate_up (ReLU):   h[r, n] = max(0, x_r . W1[e][n] + b1[e][n])
+//                     (crackedaicode "Mixture-of-Experts FFN", section
+//                     "Compute the experts and router")
+//   down:             y[r, n] = h_r . Wd[e][n] (+ b2[e][n]); the routing weight
+//                     of row r scales y, which is then added into the token's
+//                     output row (the combine of the same exercise, section
+//                     "Weight the selected outputs"), either with fp32 atomics
+//                     or into the row's own (t,k) slot for an ordered sum.
+//
+// Rows r are assignments in expert-contiguous order; tile j of the tile table
+// covers up to kGemmBM rows of one expert.  x rows are gathered through the
+// sorted token ids while they are loaded, so no permuted copy of x exists.
+// Every contraction accumulates in fp32 and the gate_up result is rounded
+// once to the compute dtype (Dew "Mixture of experts" page, section "Expert
+// computation and placement").
+//
+// Kernel shape (both dtypes): 256 threads = 2 x 2 waves; tile BM=128 rows x
+// BN=128 output columns (SwiGLU: 128 gate + 128 up weight rows); a K step is
+// 128 bytes of every row (64 bf16 or 32 fp32).  Operands go HBM -> registers ->
+// LDS (16-byte chunks, XOR-swizzled by row so MFMA fragment reads spread over
+// the banks); the next K step's global loads are in flight while the MFMAs
+// consume the current one.  Weights are MFMA operand 0 and activations operand
+// 1, so each lane's four accumulators are four consecutive output columns of
+// one row.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename Tag>
+struct Frag;
+template <>
+struct Frag<BF16> {
+  static constexpr int kEPC = 8;  // elements per 16-byte chunk
+};
+template <>
+struct Frag<F32> {
+  static constexpr int kEPC = 4;
+};
+
+template <typename Tag>
+__device__ __forceinline__ uint4 load_chunk(const typename Tag::elem* row, int64_t k, int64_t kd, bool vec) {
+  constexpr int EPC = Frag<Tag>::kEPC;
+  if (vec && k + EPC <= kd) return *reinterpret_cast<const uint4*>(row + k);
+  union {
+    typename Tag::elem e[EPC];
+    uint4 v;
+  } t;
+#pragma unroll
+  for (int j = 0; j < EPC; ++j) t.e[j] = (k + j < kd) ? row[k + j] : (typename Tag::elem)0;
+  return t.v;
+}
+
+template <typename Tag, int EPI, int BM, int BN>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
+  using elem = typename Tag::elem;
+  constexpr int EPC = Frag<Tag>::kEPC;
+  constexpr int BK = 8 * EPC;
+  constexpr bool DUAL = EPI == EPI_SWIGLU;
+  constexpr int NB = DUAL ? 2 * BN : BN;
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int SM = WTM / 16, SN = WTN / 16;
+  constexpr int LA = BM / 32, LB = NB / 32;  // 16-byte loads per thread per K step
+  constexpr int NACC = DUAL ? 2 : 1;
+
+  __shared__ uint4 As[BM * 8];
+  __shared__ uint4 Bs[NB * 8];
+
+  const int j = blockIdx.x;
+  if (j >= a.num_tiles[0]) return;
+  const int e = a.tile_e[j];
+  const int r0 = a.tile_r0[j];
+  const int rows = min(BM, a.offsets[e + 1] - r0);
+  const int64_t n0 = (int64_t)blockIdx.y * BN;
+  const int64_t N = a.N, Kd = a.Kd;
+  const bool vec = a.vec_ok != 0;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int c = tid & 7, rr = tid >> 3;
+
+  const elem* Ab = static_cast<const elem*>(a.A);
+  const elem* Bb = static_cast<const elem*>(a.B) + (int64_t)e * a.b_estride;
+  const elem* pa[LA];
+  const elem* pb[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int lr = rr + 32 * i;
+    const int r = r0 + (lr < rows ? lr : 0);
+    const int64_t src = a.a_index ? (int64_t)a.a_index[r] : (int64_t)r;
+    pa[i] = Ab + src * a.lda;
+  }
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int lb = rr + 32 * i;
+    int64_t wr;
+    if (DUAL) {
+      const int64_t nn = n0 + (lb % BN);
+      wr = (nn < N ? nn : N - 1) + (lb / BN) * a.up_off;
+    } else {
+      const int64_t nn = n0 + lb;
+      wr = nn < N ? nn : N - 1;
+    }
+    pb[i] = Bb + wr * a.ldb;
+  }
+
+  uint4 ra[LA], rb[LB];
+  auto gload = [&](int64_t k0) {
+    const int64_t k = k0 + c * EPC;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) ra[i] = load_chunk<Tag>(pa[i], k, Kd, vec);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) rb[i] = load_chunk<Tag>(pb[i], k, Kd, vec);
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int lr = rr + 32 * i;
+      As[lr * 8 + (c ^ (lr & 7))] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int lb = rr + 32 * i;
+      Bs[lb * 8 + (c ^ (lb & 7))] = rb[i];
+    }
+  };
+
+  f32x4 acc[NACC][SM][SN];
+#pragma unroll
+  for (int q = 0; q < NACC; ++q)
+#pragma unroll
+    for (int mi = 0; mi < SM; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < SN; ++ni) acc[q][mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int g = lane >> 4, l16 = lane & 15;
+  const int nk = (int)((Kd + BK - 1) / BK);
+  gload(0);
+  lstore();
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) gload((int64_t)(kt + 1) * BK);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int cc = s * 4 + g;
+      uint4 fa[SM], fb[NACC][SN];
+#pragma unroll
+      for (int mi = 0; mi < SM; ++mi) {
+        const int row = wm * WTM + mi * 16 + l16;
+        fa[mi] = As[row * 8 + (cc ^ (row & 7))];
+      }
+#pragma unroll
+      for (int q = 0; q < NACC; ++q)
+#pragma unroll
+        for (int ni = 0; ni < SN; ++ni) {
+          const int row = q * BN + wn * WTN + ni * 16 + l16;
+          fb[q][ni] = Bs[row * 8 + (cc ^ (row & 7))];
+        }
+#pragma unroll
+      for (int q = 0; q < NACC; ++q)
+#pragma unroll
+        for (int mi = 0; mi < SM; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < SN; ++ni) {
+            if constexpr (EPC == 8) {
+              acc[q][mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, fb[q][ni]), __builtin_bit_cast(bf16x8, fa[mi]), acc[q][mi][ni], 0, 0, 0);
+            } else {
+              const float4 bv = __builtin_bit_cast(float4, fb[q][ni]);
+              const float4 av = __builtin_bit_cast(float4, fa[mi]);
+              acc[q][mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv.x, av.x, acc[q][mi][ni], 0, 0, 0);
+              acc[q][mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv.y, av.y, acc[q][mi][ni], 0, 0, 0);
+              acc[q][mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv.z, av.z, acc[q][mi][ni], 0, 0, 0);
+              acc[q][mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv.w, av.w, acc[q][mi][ni], 0, 0, 0);
+            }
+          }
+    }
+    __syncthreads();
+    if (kt + 1 < nk) {
+      lstore();
+      __syncthreads();
+    }
+  }
+
+  // Epilogue.  Lane holds rows m = wm*WTM + mi*16 + l16 and columns
+  // n = n0 + wn*WTN + ni*16 + 4g + i, i = 0..3.
+  const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;
+#pragma unroll
+  for (int mi = 0; mi < SM; ++mi) {
+    const int m = wm * WTM + mi * 16 + l16;
+    if (m >= rows) continue;
+    const int r = r0 + m;
+    float wgt = 1.f;
+    int64_t orow = r;
+    if constexpr (EPI == EPI_DOWN_ATOMIC || EPI == EPI_DOWN_SLOT) {
+      wgt = a.sorted_w[r];
+      orow = (EPI == EPI_DOWN_ATOMIC) ? (int64_t)a.sorted_tok[r] : (int64_t)a.sorted_slot[r];
+    }
+#pragma unroll
+    for (int ni = 0; ni < SN; ++ni) {
+      const int64_t nb = n0 + wn * WTN + ni * 16 + 4 * g;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t n = nb + i;
+        const bool ok = n < N;
+        if constexpr (EPI == EPI_SWIGLU) {
+          float gg = acc[0][mi][ni][i], uu = acc[1][mi][ni][i];
+          if (bias && ok) {
+            gg += bias[n];
+            uu += bias[a.up_off + n];
+          }
+          v[i] = gg / (1.f + __expf(-gg)) * uu;
+        } else if constexpr (EPI == EPI_RELU) {
+          float t = acc[0][mi][ni][i];
+          if (bias && ok) t += bias[n];
+          v[i] = fmaxf(t, 0.f);
+        } else {
+          float t = acc[0][mi][ni][i];
+          if (bias && ok) t += bias[n];
+          v[i] = wgt * t;
+        }
+      }
+      if constexpr (EPI == EPI_DOWN_ATOMIC) {
+        float* dst = static_cast<float*>(a.C) + orow * a.ldc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (nb + i < N) unsafeAtomicAdd(dst + nb + i, v[i]);
+      } else if constexpr (EPI == EPI_DOWN_SLOT) {
+        float* dst = static_cast<float*>(a.C) + orow * a.ldc + nb;
+        if (nb + 4 <= N && (a.ldc & 3) == 0) {
+          *reinterpret_cast<float4*>(dst) = float4{v[0], v[1], v[2], v[3]};
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (nb + i < N) dst[i] = v[i];
+        }
+      } else {
+        elem* dst = static_cast<elem*>(a.C) + orow * a.ldc + nb;
+        if constexpr (EPC == 8) {
+          if (nb + 4 <= N && (a.ldc & 3) == 0) {
+            uint2 pk;
+            pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+            pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+            *reinterpret_cast<uint2*>(dst) = pk;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (nb + i < N) dst[i] = (uint16_t)f32_to_bf16_bits(v[i]);
+          }
+        } else {
+          if (nb + 4 <= N && (a.ldc & 3) == 0) {
+            *reinterpret_cast<float4*>(dst) = float4{v[0], v[1], v[2], v[3]};
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (nb + i < N) dst[i] = v[i];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <typename Tag, int EPI>
+hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
+  constexpr int BM = kGemmBM, BN = 128;
+  const unsigned gy = (unsigned)((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((grouped_gemm_kernel<Tag, EPI, BM, BN>), dim3(a.max_tiles, gy), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename Tag>
+hipError_t launch_tag(int epi, const GemmArgs& a, hipStream_t s) {
+  switch (epi) {
+    case EPI_SWIGLU: return launch_epi<Tag, EPI_SWIGLU>(a, s);
+    case EPI_RELU: return launch_epi<Tag, EPI_RELU>(a, s);
+    case EPI_DOWN_ATOMIC: return launch_epi<Tag, EPI_DOWN_ATOMIC>(a, s);
+    default: return launch_epi<Tag, EPI_DOWN_SLOT>(a, s);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
+  const int64_t n = a.T * a.D;
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * kThreads) {
+    const int64_t t = idx / a.D, d = idx - t * a.D;
+    float s = 0.f;
+    for (int k = 0; k < a.K; ++k) s += a.src[(t * a.K + k) * a.D + d];
+    if (a.out_bf16)
+      static_cast<uint16_t*>(a.out)[idx] = (uint16_t)f32_to_bf16_bits(s);
+    else
+      static_cast<float*>(a.out)[idx] = s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
+  if (a.max_tiles <= 0 || a.N <= 0) return hipSuccess;
+  return dtype == 1 ? launch_tag<BF16>(epi, a, s) : launch_tag<F32>(epi, a, s);
+}
+
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
+  const int64_t n = a.T * a.D;
+  if (n <= 0) return hipSuccess;
+  const int64_t want = (n + kThreads - 1) / kThreads;
+  const unsigned grid = (unsigned)(want < 16384 ? want : 16384);
+  hipLaunchKernelGGL(finalize_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

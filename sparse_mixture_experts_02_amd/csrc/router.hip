@@ -1,0 +1,270 @@
+// Router kernel: logits = x . router^T (+ bias), softmax over the experts,
+// top-k in descending order with ties to the lower expert index, and the
+// routing weights p_sel / (sum p_sel + 1e-9) when renormalising (mojolearn
+// "MoEBlock" class description; crackedaicode "Mixture-of-Experts FFN",
+// sections "Compute the experts and router" and "Weight the selected
+// outputs").
+//
+// One block of 256 threads (4 waves) owns 16 tokens.
+//  * Logits: an MFMA product with the experts as the 16-wide MFMA rows and the
+//    16 tokens as its columns.  The four waves split the model width D into
+//    four ranges (split-K) and their partial sums meet in LDS, so one block
+//    reads its 16 token rows exactly once straight from HBM into registers.
+//  * Selection: L lanes per token (L = E rounded up to a power of two, at most
+//    64), each lane holding up to four experts.  Maximum, sum and the K
+//    top-k rounds are xor-shuffle reductions inside the L-lane group.  The
+//    top-k key packs (probability bits << 32) | (0xffffffff - expert): since
+//    probabilities are >= 0 their bit patterns order like the values, and the
+//    larger key on equal probabilities is the lower expert index.
+//  * The same block clears the rows of the fp32 combine buffer for its tokens
+//    (the down projection adds into them with atomics).
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* row, int64_t k, int64_t n, bool vec) {
+  if (vec && k + 8 <= n) {
+    uint4 v = *reinterpret_cast<const uint4*>(row + k);
+    return __builtin_bit_cast(bf16x8, v);
+  }
+  union {
+    uint16_t h[8];
+    uint4 v;
+  } t;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) t.h[j] = (k + j < n) ? row[k + j] : (uint16_t)0;
+  return __builtin_bit_cast(bf16x8, t.v);
+}
+
+__device__ __forceinline__ float4 load_f32x4(const float* row, int64_t k, int64_t n, bool vec) {
+  if (vec && k + 4 <= n) return *reinterpret_cast<const float4*>(row + k);
+  float4 v;
+  v.x = (k + 0 < n) ? row[k + 0] : 0.f;
+  v.y = (k + 1 < n) ? row[k + 1] : 0.f;
+  v.z = (k + 2 < n) ? row[k + 2] : 0.f;
+  v.w = (k + 3 < n) ? row[k + 3] : 0.f;
+  return v;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Partial logits of this wave's D range: acc[nt][i] = sum over the range of
+// x[t0 + lane%16] . router[nt*16 + 4*(lane/16) + i].
+template <typename Tag, int NT>
+__device__ __forceinline__ void logits_partial(const RouterArgs& a, int64_t t0, int w, int lane, f32x4 (&acc)[NT]) {
+  const int64_t D = a.D;
+  const int64_t tok = min(t0 + (lane & 15), a.T - 1);
+  const int g = lane >> 4;
+  const bool vec = a.vec_ok != 0;
+  int64_t erow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) erow[nt] = min(nt * 16 + (lane & 15), a.E - 1);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // U k-steps per iteration: all their loads are issued before the MFMAs so
+  // several HBM round trips overlap.  Elements at or past ke read as zero.
+  constexpr int U = NT <= 2 ? 4 : (NT <= 4 ? 2 : 1);
+  if constexpr (sizeof(typename Tag::elem) == 2) {
+    constexpr int KS = 32;
+    const int64_t steps = (D + KS - 1) / KS;
+    const int64_t per = (steps + 3) / 4;
+    const int64_t kb = w * per * KS, ke = min(D, (w + 1) * per * KS);
+    const uint16_t* xr = static_cast<const uint16_t*>(a.x) + tok * D;
+    const uint16_t* R = static_cast<const uint16_t*>(a.router);
+    for (int64_t k = kb; k < ke; k += U * KS) {
+      bf16x8 xa[U], rb[U][NT];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t kk = k + u * KS + 8 * g;
+        xa[u] = load_bf16x8(xr, kk, ke, vec);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) rb[u][nt] = load_bf16x8(R + erow[nt] * D, kk, ke, vec);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb[u][nt], xa[u], acc[nt], 0, 0, 0);
+    }
+  } else {
+    constexpr int KS = 16;
+    const int64_t steps = (D + KS - 1) / KS;
+    const int64_t per = (steps + 3) / 4;
+    const int64_t kb = w * per * KS, ke = min(D, (w + 1) * per * KS);
+    const float* xr = static_cast<const float*>(a.x) + tok * D;
+    const float* R = static_cast<const float*>(a.router);
+    for (int64_t k = kb; k < ke; k += U * KS) {
+      float4 xa[U], rv[U][NT];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t kk = k + u * KS + 4 * g;
+        xa[u] = load_f32x4(xr, kk, ke, vec);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) rv[u][nt] = load_f32x4(R + erow[nt] * D, kk, ke, vec);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(rv[u][nt].x, xa[u].x, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(rv[u][nt].y, xa[u].y, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(rv[u][nt].z, xa[u].z, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(rv[u][nt].w, xa[u].w, acc[nt], 0, 0, 0);
+        }
+    }
+  }
+}
+
+template <typename Tag, int NT>
+__global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
+  constexpr int EP = NT * 16;
+  extern __shared__ float part[];  // [4 waves][16 tokens][EP]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * kRouterTokens;
+  const int E = a.E, K = a.K;
+
+  // Clear this block's rows of the combine buffer.
+  if (a.zero_rows) {
+    const int64_t cols = a.zero_cols;
+    const int64_t rows = min((int64_t)kRouterTokens, a.T - t0);
+    float* z = a.zero_rows + t0 * cols;
+    const int64_t n = rows * cols;
+    if ((cols & 3) == 0) {
+      for (int64_t i = (int64_t)tid * 4; i < n; i += kThreads * 4)
+        *reinterpret_cast<float4*>(z + i) = float4{0.f, 0.f, 0.f, 0.f};
+    } else {
+      for (int64_t i = tid; i < n; i += kThreads) z[i] = 0.f;
+    }
+  }
+
+  f32x4 acc[NT];
+  logits_partial<Tag, NT>(a, t0, w, lane, acc);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[(w * 16 + (lane & 15)) * EP + nt * 16 + 4 * (lane >> 4) + i] = acc[nt][i];
+  __syncthreads();
+
+  // Sum the four partials; add the bias; publish the logits.
+  for (int idx = tid; idx < 16 * EP; idx += kThreads) {
+    const int tk = idx / EP, e = idx % EP;
+    float v = part[idx] + part[16 * EP + idx] + part[32 * EP + idx] + part[48 * EP + idx];
+    if (e < E && a.router_bias) v += a.router_bias[e];
+    part[idx] = v;
+    if (a.logits && e < E && t0 + tk < a.T) a.logits[(t0 + tk) * E + e] = v;
+  }
+  __syncthreads();
+
+  // Softmax and top-k with L lanes per token.
+  int L = 1;
+  while (L < E && L < 64) L <<= 1;
+  const int per_wave = 64 / L;      // tokens one wave pass covers
+  const int j = lane % L;           // lane inside the token's group
+  for (int base = 0; base < 4; base += per_wave) {
+    const int slot = base + lane / L;          // 0..3 inside this wave's four tokens
+    const int tk = w * 4 + slot;
+    const bool active = (slot < 4) && (t0 + tk < a.T);
+    const float* lg = part + (active ? tk : w * 4) * EP;
+
+    float lv[4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = j + i * L;
+      lv[i] = (e < E) ? lg[e] : -INFINITY;
+      m = fmaxf(m, lv[i]);
+    }
+    for (int o = L >> 1; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float ev[4], s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = j + i * L;
+      ev[i] = (e < E) ? expf(lv[i] - m) : 0.f;
+      s += ev[i];
+    }
+    for (int o = L >> 1; o > 0; o >>= 1) s += __shfl_xor(s, o);
+
+    uint64_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = j + i * L;
+      key[i] = (e < E) ? (((uint64_t)__float_as_uint(ev[i] / s) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
+    }
+
+    float psum = 0.f;
+    int mysel[4] = {0, 0, 0, 0};
+    float myp[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < K; ++k) {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+      for (int o = L >> 1; o > 0; o >>= 1) {
+        const uint64_t other = shfl_xor_u64(best, o);
+        best = other > best ? other : best;
+      }
+      const int e = (int)(0xffffffffu - (uint32_t)best);
+      const float p = __uint_as_float((uint32_t)(best >> 32));
+      psum += p;
+      if (e % L == j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (e / L == i) key[i] = 0ull;
+      }
+      const int kq = k / L, kr = k % L;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (kq == i && kr == j) {
+          mysel[i] = e;
+          myp[i] = p;
+        }
+    }
+    if (active) {
+      const float denom = psum + 1e-9f;
+      const int64_t t = t0 + tk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = j + i * L;
+        if (k < K) {
+          a.sel64[t * K + k] = mysel[i];
+          a.sel32[t * K + k] = mysel[i];
+          a.weights[t * K + k] = a.norm ? myp[i] / denom : myp[i];
+        }
+      }
+    }
+  }
+}
+
+template <typename Tag, int NT>
+hipError_t launch_nt(const RouterArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)((a.T + kRouterTokens - 1) / kRouterTokens);
+  const size_t lds = (size_t)4 * 16 * NT * 16 * sizeof(float);
+  hipLaunchKernelGGL((router_kernel<Tag, NT>), dim3(grid), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <typename Tag>
+hipError_t launch_tag(const RouterArgs& a, hipStream_t s) {
+  const int nt = (a.E + 15) / 16;
+  if (nt <= 1) return launch_nt<Tag, 1>(a, s);
+  if (nt <= 2) return launch_nt<Tag, 2>(a, s);
+  if (nt <= 4) return launch_nt<Tag, 4>(a, s);
+  if (nt <= 8) return launch_nt<Tag, 8>(a, s);
+  return launch_nt<Tag, 16>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_router(int dtype, const RouterArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  return dtype == 1 ? launch_tag<BF16>(a, s) : launch_tag<F32>(a, s);
+}
+
+}  // namespace moe

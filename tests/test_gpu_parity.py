@@ -1,0 +1,256 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Every call goes through the C ABI (ctypes binding over libmoe.so).  Sizes:
+the small workloads are compared token by token in full; the full-size
+workloads (the Mixtral-shaped prefill and decode, the 128-expert layer) run
+at their real shape in the configuration the benchmark times and are compared
+on sampled tokens, plus properties that hold for every token.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import workloads
+from parity import check, check_full_properties, device_inputs, gpu_forward, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no ROCm device", allow_module_level=True)
+
+import sparse_mixture_experts_02_amd as moe  # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _say(msg):
+    print("[gpu-parity] " + msg, flush=True)
+
+
+def _sample(T, n, seed=0):
+    rng = np.random.default_rng(seed)
+    s = rng.choice(T, size=min(n, T), replace=False)
+    return np.unique(np.concatenate([s, [0, T - 1]]))
+
+
+# ------------------------------------------------------------ small, full
+@pytest.mark.parametrize("det", [False, True])
+def test_tiny_block_fp32(det):
+    inp = workloads.generate("tiny")
+    _say("tiny det=%s" % det)
+    g = gpu_forward(inp, deterministic=det)
+    st = check(inp, g)
+    check_full_properties(inp, g)
+    _say(str(st))
+
+
+def test_relu_experts_fp32_full():
+    inp = workloads.generate("relu")
+    _say("relu T=4096 D=512 F=2048")
+    g = gpu_forward(inp)
+    st = check(inp, g)
+    check_full_properties(inp, g)
+    _say(str(st))
+
+
+def test_worked_example_on_gpu():
+    """The exercise's two-token example through the whole GPU layer: a ReLU
+    layer whose router rows hold ln p and whose experts reproduce the printed
+    expert outputs (crackedaicode "Mixture-of-Experts FFN", "Work through two
+    tokens")."""
+    from test_oracle_pins import worked_example_layer
+    lay, g = worked_example_layer()
+    d = {k: to_device(v) for k, v in lay.items()}
+    out, sel, w = moe.forward(d["x"], d["router"], d["gate_up"], d["down"], top_k=2, act="relu")
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), np.array(g["expected_indices"]))
+    np.testing.assert_allclose(out.cpu().numpy(), np.array(g["expected_out"]), rtol=0, atol=g["atol"])
+
+
+EDGE = [
+    # (T, D, F, E, K, act, dtype, biases, norm)
+    (1, 64, 128, 8, 2, "swiglu", "f32", False, True),
+    (300, 72, 200, 6, 2, "swiglu", "f32", False, True),
+    (300, 72, 200, 6, 2, "swiglu", "bf16", False, True),
+    (257, 13, 9, 5, 3, "swiglu", "f32", True, True),
+    (257, 13, 9, 5, 3, "relu", "bf16", True, False),
+    (1000, 128, 256, 4, 2, "swiglu", "bf16", False, True),
+    (513, 96, 160, 3, 3, "relu", "f32", True, True),
+    (200, 64, 64, 1, 1, "swiglu", "bf16", False, True),
+    (333, 40, 48, 7, 1, "swiglu", "f32", False, False),
+    (129, 256, 96, 256, 4, "swiglu", "bf16", False, True),
+    (2048, 256, 512, 16, 4, "relu", "bf16", True, True),
+    (77, 8, 8, 37, 37, "swiglu", "f32", False, True),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: "T%d_D%d_F%d_E%d_K%d_%s_%s_b%d_n%d" % tuple(c))
+@pytest.mark.parametrize("det", [False, True])
+def test_edge_shapes(case, det):
+    T, D, F, E, K, act, dt, biases, norm = case
+    cfg = workloads.small_config(T, D, F, E, K, act=act, dtype=dt, norm=norm, biases=biases,
+                                 router_bias="zipf" if E >= 8 else None, cfg_id=200 + E + K)
+    inp = workloads.generate(cfg)
+    _say("edge %s det=%s" % (case, det))
+    g = gpu_forward(inp, deterministic=det)
+    check(inp, g)
+    check_full_properties(inp, g)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_small_sweep(seed):
+    rng = np.random.default_rng(seed)
+    E = int(rng.integers(1, 12))
+    K = int(rng.integers(1, E + 1))
+    cfg = workloads.small_config(int(rng.integers(1, 200)), int(rng.integers(1, 80)), int(rng.integers(1, 80)),
+                                 E, K, act=["swiglu", "relu"][seed % 2], dtype=["f32", "bf16"][(seed // 2) % 2],
+                                 norm=bool(seed % 3), biases=bool(seed % 4 == 1), cfg_id=300 + seed)
+    inp = workloads.generate(cfg)
+    _say("sweep seed=%d cfg=%s" % (seed, {k: cfg[k] for k in ("T", "D", "F", "E", "K", "act", "dtype")}))
+    g = gpu_forward(inp, deterministic=bool(seed % 2))
+    check(inp, g)
+    check_full_properties(inp, g)
+
+
+def test_bf16_output():
+    cfg = workloads.small_config(400, 128, 192, 8, 2, dtype="bf16", cfg_id=400)
+    inp = workloads.generate(cfg)
+    for det in (False, True):
+        g = gpu_forward(inp, deterministic=det, out_dtype=torch.bfloat16)
+        check(inp, g, out_bf16=True)
+
+
+def test_zero_tokens():
+    d = device_inputs(workloads.generate(workloads.small_config(4, 16, 16, 4, 2, cfg_id=401)))
+    out, sel, w = moe.forward(d["x"][:0], d["router"], d["gate_up"], d["down"], top_k=2)
+    assert out.shape == (0, 16) and sel.shape == (0, 2)
+
+
+def test_errors_map_to_python_exceptions():
+    d = device_inputs(workloads.generate(workloads.small_config(4, 16, 16, 4, 2, cfg_id=402)))
+    with pytest.raises(ValueError):
+        moe.forward(d["x"], d["router"], d["gate_up"], d["down"], top_k=0)
+    with pytest.raises(ValueError):
+        moe.forward(d["x"], d["router"], d["gate_up"], d["down"], top_k=5)
+    with pytest.raises(NotImplementedError):
+        moe.forward(d["x"], d["router"], d["gate_up"], d["down"], top_k=2, act="gelu")
+    with pytest.raises(TypeError):
+        moe.forward(d["x"].double(), d["router"], d["gate_up"], d["down"], top_k=2)
+    with pytest.raises(ValueError):
+        moe.forward(d["x"], d["router"], d["gate_up"][:, :8], d["down"], top_k=2)
+
+
+def test_deterministic_runs_are_bitwise_identical():
+    cfg = workloads.small_config(1500, 128, 256, 16, 4, dtype="bf16", router_bias="zipf", cfg_id=403)
+    inp = workloads.generate(cfg)
+    d = device_inputs(inp)
+    a = gpu_forward(inp, d, deterministic=True)
+    b = gpu_forward(inp, d, deterministic=True)
+    assert np.array_equal(a["out"], b["out"])
+    # K = 2 atomics onto a zeroed buffer are also reproducible (0 + a + b = 0 + b + a).
+    cfg2 = dict(cfg, K=2)
+    inp2 = workloads.generate(cfg2)
+    d2 = device_inputs(inp2)
+    a2 = gpu_forward(inp2, d2)
+    b2 = gpu_forward(inp2, d2)
+    assert np.array_equal(a2["out"], b2["out"])
+
+
+def test_dispatch_is_a_stable_counting_sort():
+    cfg = workloads.small_config(3000, 64, 64, 24, 3, dtype="bf16", router_bias="zipf", cfg_id=404)
+    inp = workloads.generate(cfg)
+    d = device_inputs(inp)
+    r = moe.dispatch(d["x"], d["router"], top_k=3, router_bias=d["router_bias"])
+    torch.cuda.synchronize()
+    sel = r["selected_experts"].cpu().numpy()
+    counts = r["expert_counts"].cpu().numpy()
+    offs = r["expert_offsets"].cpu().numpy()
+    tok = r["sorted_token"].cpu().numpy()
+    slot = r["sorted_slot"].cpu().numpy()
+    flat = sel.ravel()
+    assert np.array_equal(counts, np.bincount(flat, minlength=24))
+    assert np.array_equal(offs, np.concatenate([[0], np.cumsum(counts)]))
+    # stable: exactly a stable argsort of the flattened expert ids
+    order = np.argsort(flat, kind="stable")
+    assert np.array_equal(slot, order)
+    assert np.array_equal(tok, order // 3)
+    # the same router kernel as the full forward
+    assert np.array_equal(sel, gpu_forward(inp, d)["sel"])
+
+
+# ----------------------------------------------------- full-size workloads
+_CACHE = {}
+
+
+def _inputs(name):
+    if name not in _CACHE:
+        _CACHE.clear()
+        _say("generating %s" % name)
+        _CACHE[name] = workloads.generate(name)
+    return _CACHE[name]
+
+
+def _prefill_family():
+    if "prefill" not in _CACHE:
+        _CACHE.clear()
+        _say("generating prefill")
+        _CACHE["prefill"] = workloads.generate("prefill")
+    return _CACHE["prefill"]
+
+
+@pytest.mark.slow
+def test_prefill_mixtral_shape_sampled():
+    inp = _prefill_family()
+    d = device_inputs(inp)
+    _say("prefill T=8192 D=4096 F=14336 E=8 K=2 bf16")
+    g = gpu_forward(inp, d)
+    check_full_properties(inp, g)
+    st = check(inp, g, tokens=_sample(8192, 48))
+    _say(str(st))
+    _CACHE["prefill_dev"] = d
+    _CACHE["prefill_gpu"] = g
+
+
+@pytest.mark.slow
+def test_decode_mixtral_shape_full():
+    base = _prefill_family()
+    inp = dict(base, cfg=dict(base["cfg"], T=64), x=base["x"][:64])
+    d = _CACHE.get("prefill_dev") or device_inputs(base)
+    dd = dict(d, x=d["x"][:64].contiguous())
+    _say("decode T=64 D=4096 F=14336 E=8 K=2 bf16")
+    g = gpu_forward(inp, dd)
+    check_full_properties(inp, g)
+    st = check(inp, g)
+    _say(str(st))
+    # the decode batch is the first 64 prefill tokens: same routing and output
+    if "prefill_gpu" in _CACHE:
+        pg = _CACHE["prefill_gpu"]
+        assert np.array_equal(g["sel"], pg["sel"][:64])
+        rms = np.sqrt(np.mean(pg["out"][:64] ** 2))
+        assert np.abs(g["out"] - pg["out"][:64]).max() <= 1e-3 * rms
+    _CACHE.pop("prefill_dev", None)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["fine", "fine_zero"])
+def test_fine_grained_128_experts_sampled(name):
+    inp = _inputs(name)
+    d = device_inputs(inp)
+    _say("%s T=16384 D=2048 F=768 E=128 K=8 bf16" % name)
+    g = gpu_forward(inp, d, deterministic=name == "fine_zero")
+    check_full_properties(inp, g)
+    st = check(inp, g, tokens=_sample(16384, 96, seed=1))
+    _say(str(st))
+    if name == "fine_zero":
+        z = workloads.zero_load_experts(128)
+        assert np.all(g["counts"][z] == 0)
+        # Poison the experts no token reaches: the output must not change.
+        gu, dn = d["gate_up"].clone(), d["down"].clone()
+        zt = torch.from_numpy(z).to(gu.device)
+        gu[zt] = float("nan")
+        dn[zt] = float("nan")
+        g2 = gpu_forward(inp, dict(d, gate_up=gu, down=dn), deterministic=True)
+        assert np.array_equal(g2["out"], g["out"])
+    _CACHE.pop(name, None)
