@@ -111,6 +111,24 @@ moe_status moe_forward(const moe_desc* d, const void* x, const void* router, con
                        void* stream);
 
 /*
+ * moe_forward_timed -- moe_forward that also records caller-created HIP events
+ * (hipEvent_t handles passed as void*) on `stream` at its stage boundaries, so
+ * a caller can time each stage with hipEventElapsedTime.  events[0] is
+ * recorded before the router, [1] after the router, [2] after the sort into
+ * expert order, [3] after the gate_up GEMM, [4] after the down GEMM and [5]
+ * after the finalize step (recorded right after [4] when there is none).
+ * Only the first min(n_events, MOE_STAGE_EVENTS) are recorded; events may be
+ * NULL.  Everything else is exactly moe_forward.
+ */
+#define MOE_STAGE_EVENTS 6
+moe_status moe_forward_timed(const moe_desc* d, const void* x, const void* router, const void* gate_up_proj,
+                             const void* down_proj, const float* router_bias, const float* up_bias,
+                             const float* down_bias, void* out, int64_t* selected_experts,
+                             float* routing_weights, float* router_logits, int32_t* expert_counts,
+                             void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                             int32_t n_events);
+
+/*
  * moe_dispatch -- the router and the sort into expert order alone (the
  * "global" dispatch of the Dew page: tokens sorted into expert order so each
  * expert's rows are contiguous).  The order is stable: inside an expert's

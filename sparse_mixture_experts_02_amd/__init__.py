@@ -56,6 +56,12 @@ def load_library():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("libmoe.so is not built: run `python -m sparse_mixture_experts_02_amd.build` "
                                "(the layer has no non-HIP fallback)")
+        # Load torch's HIP runtime first so the library binds to that same
+        # runtime instance (one set of streams and allocations per process).
+        try:
+            import torch  # noqa: F401
+        except ImportError:  # pragma: no cover
+            pass
         lib = ctypes.CDLL(LIB_PATH)
         P, S, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
         D = ctypes.POINTER(MoeDesc)
@@ -63,6 +69,8 @@ def load_library():
         lib.moe_workspace_bytes.restype = ctypes.c_int
         lib.moe_forward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
         lib.moe_forward.restype = ctypes.c_int
+        lib.moe_forward_timed.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P, P, I32]
+        lib.moe_forward_timed.restype = ctypes.c_int
         lib.moe_dispatch.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
         lib.moe_dispatch.restype = ctypes.c_int
         lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -95,6 +103,16 @@ def moe_forward(desc, x, router, gate_up_proj, down_proj, router_bias, up_bias, 
     return load_library().moe_forward(ctypes.byref(desc), x, router, gate_up_proj, down_proj, router_bias, up_bias,
                                       down_bias, out, selected_experts, routing_weights, router_logits,
                                       expert_counts, workspace, workspace_bytes, stream)
+
+
+def moe_forward_timed(desc, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out,
+                      selected_experts, routing_weights, router_logits, expert_counts, workspace, workspace_bytes,
+                      stream, events, n_events) -> int:
+    """Raw call of moe_forward_timed; ``events`` is a ctypes array of hipEvent_t handles (or None)."""
+    return load_library().moe_forward_timed(ctypes.byref(desc), x, router, gate_up_proj, down_proj, router_bias,
+                                            up_bias, down_bias, out, selected_experts, routing_weights,
+                                            router_logits, expert_counts, workspace, workspace_bytes, stream,
+                                            events, n_events)
 
 
 def moe_dispatch(desc, x, router, router_bias, selected_experts, routing_weights, router_logits, expert_counts,
@@ -238,5 +256,7 @@ def dispatch(x, router, *, top_k, norm_topk_prob=True, router_bias=None, num_exp
     return r
 
 
-__all__ = ["MoeDesc", "MoEError", "load_library", "moe_forward", "moe_dispatch", "moe_workspace_bytes",
+MOE_STAGE_EVENTS = 6
+
+__all__ = ["MoeDesc", "MoEError", "load_library", "moe_forward", "moe_forward_timed", "moe_dispatch", "moe_workspace_bytes",
            "moe_status_string", "moe_abi_version", "make_desc", "forward", "dispatch", "LIB_PATH"]

@@ -81,10 +81,21 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+// Records events[i] on s when the caller asked for it.
+struct Marks {
+  void* const* ev;
+  int32_t n;
+  hipStream_t s;
+  bool mark(int i) const {
+    if (!ev || i >= n || !ev[i]) return true;
+    return hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) == hipSuccess;
+  }
+};
+
 moe_status route_and_sort(const moe_desc* d, const Layout& L, const void* x, const void* router,
                           const float* router_bias, int64_t* sel, float* weights, float* logits,
                           int32_t* counts_out, int32_t* offsets_out, int32_t* sorted_tok, int32_t* sorted_slot,
-                          float* zero_rows, void* ws, hipStream_t s) {
+                          float* zero_rows, void* ws, hipStream_t s, const Marks& mk) {
   const int eb = elem_bytes(d->dtype);
   RouterArgs ra{};
   ra.x = x;
@@ -102,7 +113,7 @@ moe_status route_and_sort(const moe_desc* d, const Layout& L, const void* x, con
   ra.zero_rows = zero_rows;
   ra.zero_cols = d->D;
   ra.vec_ok = aligned16(x) && aligned16(router) && ((d->D * eb) % 16 == 0);
-  if (launch_router(d->dtype, ra, s) != hipSuccess) return MOE_EDEVICE;
+  if (launch_router(d->dtype, ra, s) != hipSuccess || !mk.mark(1)) return MOE_EDEVICE;
 
   DispatchArgs da{};
   da.sel32 = ra.sel32;
@@ -125,7 +136,93 @@ moe_status route_and_sort(const moe_desc* d, const Layout& L, const void* x, con
   da.tile_e = at<int32_t>(ws, L.tile_e);
   da.tile_r0 = at<int32_t>(ws, L.tile_r0);
   da.num_tiles = at<int32_t>(ws, L.num_tiles);
-  if (launch_dispatch(da, s) != hipSuccess) return MOE_EDEVICE;
+  if (launch_dispatch(da, s) != hipSuccess || !mk.mark(2)) return MOE_EDEVICE;
+  return MOE_OK;
+}
+
+moe_status forward_impl(const moe_desc* d, const void* x, const void* router, const void* gate_up_proj,
+                        const void* down_proj, const float* router_bias, const float* up_bias,
+                        const float* down_bias, void* out, int64_t* selected_experts, float* routing_weights,
+                        float* router_logits, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                        void* stream, void* const* events, int32_t n_events) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!x || !router || !gate_up_proj || !down_proj || !out || !selected_experts || !routing_weights || !workspace)
+    return MOE_EINVAL;
+  const Layout L = layout_of(d);
+  if (workspace_bytes < L.total) return MOE_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Marks mk{events, n_events, s};
+  const int eb = elem_bytes(d->dtype);
+  const bool swiglu = d->act == MOE_ACT_SWIGLU;
+  const int64_t G = swiglu ? 2 : 1;
+
+  // The fp32 buffer the down projection adds into (atomic mode).
+  float* acc = nullptr;
+  if (!d->deterministic) acc = d->out_dtype == MOE_F32 ? static_cast<float*>(out) : at<float>(workspace, L.acc);
+
+  if (!mk.mark(0)) return MOE_EDEVICE;
+  st = route_and_sort(d, L, x, router, router_bias, selected_experts, routing_weights, router_logits, expert_counts,
+                      nullptr, nullptr, nullptr, acc, workspace, s, mk);
+  if (st != MOE_OK) return st;
+
+  GemmArgs g{};
+  g.A = x;
+  g.lda = d->D;
+  g.a_index = at<int32_t>(workspace, L.sorted_tok);
+  g.B = gate_up_proj;
+  g.ldb = d->D;
+  g.b_estride = G * d->F * d->D;
+  g.up_off = d->F;
+  g.N = d->F;
+  g.Kd = d->D;
+  g.tile_e = at<int32_t>(workspace, L.tile_e);
+  g.tile_r0 = at<int32_t>(workspace, L.tile_r0);
+  g.num_tiles = at<int32_t>(workspace, L.num_tiles);
+  g.offsets = at<int32_t>(workspace, L.offsets);
+  g.max_tiles = L.max_tiles;
+  g.bias = up_bias;
+  g.bias_estride = G * d->F;
+  g.C = at<void>(workspace, L.h);
+  g.ldc = d->F;
+  g.sorted_tok = at<int32_t>(workspace, L.sorted_tok);
+  g.sorted_slot = at<int32_t>(workspace, L.sorted_slot);
+  g.sorted_w = at<float>(workspace, L.sorted_w);
+  g.vec_ok = aligned16(x) && aligned16(gate_up_proj) && ((d->D * eb) % 16 == 0);
+  if (launch_grouped_gemm(d->dtype, swiglu ? EPI_SWIGLU : EPI_RELU, g, s) != hipSuccess || !mk.mark(3))
+    return MOE_EDEVICE;
+
+  GemmArgs h = g;
+  h.A = at<void>(workspace, L.h);
+  h.lda = d->F;
+  h.a_index = nullptr;
+  h.B = down_proj;
+  h.ldb = d->F;
+  h.b_estride = d->D * d->F;
+  h.up_off = 0;
+  h.N = d->D;
+  h.Kd = d->F;
+  h.bias = down_bias;
+  h.bias_estride = d->D;
+  h.C = d->deterministic ? at<void>(workspace, L.slots) : static_cast<void*>(acc);
+  h.ldc = d->D;
+  h.vec_ok = aligned16(down_proj) && ((d->F * eb) % 16 == 0);
+  if (launch_grouped_gemm(d->dtype, d->deterministic ? EPI_DOWN_SLOT : EPI_DOWN_ATOMIC, h, s) != hipSuccess ||
+      !mk.mark(4))
+    return MOE_EDEVICE;
+
+  if (d->deterministic || d->out_dtype == MOE_BF16) {
+    FinalizeArgs f{};
+    f.src = d->deterministic ? at<float>(workspace, L.slots) : acc;
+    f.out = out;
+    f.T = d->T;
+    f.D = d->D;
+    f.K = d->deterministic ? d->K : 1;
+    f.out_bf16 = d->out_dtype == MOE_BF16;
+    if (launch_finalize(f, s) != hipSuccess) return MOE_EDEVICE;
+  }
+  if (!mk.mark(5)) return MOE_EDEVICE;
   return MOE_OK;
 }
 
@@ -160,80 +257,19 @@ moe_status moe_forward(const moe_desc* d, const void* x, const void* router, con
                        const float* down_bias, void* out, int64_t* selected_experts, float* routing_weights,
                        float* router_logits, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  moe_status st = check_desc(d);
-  if (st != MOE_OK) return st;
-  if (d->T == 0) return MOE_OK;
-  if (!x || !router || !gate_up_proj || !down_proj || !out || !selected_experts || !routing_weights || !workspace)
-    return MOE_EINVAL;
-  const Layout L = layout_of(d);
-  if (workspace_bytes < L.total) return MOE_EWORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int eb = elem_bytes(d->dtype);
-  const bool swiglu = d->act == MOE_ACT_SWIGLU;
-  const int64_t G = swiglu ? 2 : 1;
+  return forward_impl(d, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out, selected_experts,
+                      routing_weights, router_logits, expert_counts, workspace, workspace_bytes, stream, nullptr, 0);
+}
 
-  // The fp32 buffer the down projection adds into (atomic mode).
-  float* acc = nullptr;
-  if (!d->deterministic) acc = d->out_dtype == MOE_F32 ? static_cast<float*>(out) : at<float>(workspace, L.acc);
-
-  st = route_and_sort(d, L, x, router, router_bias, selected_experts, routing_weights, router_logits, expert_counts,
-                      nullptr, nullptr, nullptr, acc, workspace, s);
-  if (st != MOE_OK) return st;
-
-  GemmArgs g{};
-  g.A = x;
-  g.lda = d->D;
-  g.a_index = at<int32_t>(workspace, L.sorted_tok);
-  g.B = gate_up_proj;
-  g.ldb = d->D;
-  g.b_estride = G * d->F * d->D;
-  g.up_off = d->F;
-  g.N = d->F;
-  g.Kd = d->D;
-  g.tile_e = at<int32_t>(workspace, L.tile_e);
-  g.tile_r0 = at<int32_t>(workspace, L.tile_r0);
-  g.num_tiles = at<int32_t>(workspace, L.num_tiles);
-  g.offsets = at<int32_t>(workspace, L.offsets);
-  g.max_tiles = L.max_tiles;
-  g.bias = up_bias;
-  g.bias_estride = G * d->F;
-  g.C = at<void>(workspace, L.h);
-  g.ldc = d->F;
-  g.sorted_tok = at<int32_t>(workspace, L.sorted_tok);
-  g.sorted_slot = at<int32_t>(workspace, L.sorted_slot);
-  g.sorted_w = at<float>(workspace, L.sorted_w);
-  g.vec_ok = aligned16(x) && aligned16(gate_up_proj) && ((d->D * eb) % 16 == 0);
-  if (launch_grouped_gemm(d->dtype, swiglu ? EPI_SWIGLU : EPI_RELU, g, s) != hipSuccess) return MOE_EDEVICE;
-
-  GemmArgs h = g;
-  h.A = at<void>(workspace, L.h);
-  h.lda = d->F;
-  h.a_index = nullptr;
-  h.B = down_proj;
-  h.ldb = d->F;
-  h.b_estride = d->D * d->F;
-  h.up_off = 0;
-  h.N = d->D;
-  h.Kd = d->F;
-  h.bias = down_bias;
-  h.bias_estride = d->D;
-  h.C = d->deterministic ? at<void>(workspace, L.slots) : static_cast<void*>(acc);
-  h.ldc = d->D;
-  h.vec_ok = aligned16(down_proj) && ((d->F * eb) % 16 == 0);
-  if (launch_grouped_gemm(d->dtype, d->deterministic ? EPI_DOWN_SLOT : EPI_DOWN_ATOMIC, h, s) != hipSuccess)
-    return MOE_EDEVICE;
-
-  if (d->deterministic || d->out_dtype == MOE_BF16) {
-    FinalizeArgs f{};
-    f.src = d->deterministic ? at<float>(workspace, L.slots) : acc;
-    f.out = out;
-    f.T = d->T;
-    f.D = d->D;
-    f.K = d->deterministic ? d->K : 1;
-    f.out_bf16 = d->out_dtype == MOE_BF16;
-    if (launch_finalize(f, s) != hipSuccess) return MOE_EDEVICE;
-  }
-  return MOE_OK;
+moe_status moe_forward_timed(const moe_desc* d, const void* x, const void* router, const void* gate_up_proj,
+                             const void* down_proj, const float* router_bias, const float* up_bias,
+                             const float* down_bias, void* out, int64_t* selected_experts,
+                             float* routing_weights, float* router_logits, int32_t* expert_counts,
+                             void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                             int32_t n_events) {
+  return forward_impl(d, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out, selected_experts,
+                      routing_weights, router_logits, expert_counts, workspace, workspace_bytes, stream, events,
+                      n_events);
 }
 
 moe_status moe_dispatch(const moe_desc* d, const void* x, const void* router, const float* router_bias,
@@ -248,9 +284,10 @@ moe_status moe_dispatch(const moe_desc* d, const void* x, const void* router, co
     return MOE_EINVAL;
   const Layout L = layout_of(d);
   if (workspace_bytes < L.total) return MOE_EWORKSPACE;
+  const Marks none{nullptr, 0, nullptr};
   return route_and_sort(d, L, x, router, router_bias, selected_experts, routing_weights, router_logits,
                         expert_counts, expert_offsets, sorted_token, sorted_slot, nullptr, workspace,
-                        static_cast<hipStream_t>(stream));
+                        static_cast<hipStream_t>(stream), none);
 }
 
 }  // extern "C"
