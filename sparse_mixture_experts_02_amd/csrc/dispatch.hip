@@ -6,7 +6,7 @@
 //   count   one block per chunk of 1024 assignments: LDS histogram per expert
 //   scan    one block: per-expert totals, the exclusive scan into segment
 //           offsets, each chunk's starting row inside every segment, and the
-//           tile table of the grouped GEMMs (empty experts get no tile, so
+//           work lists of the grouped GEMMs (empty experts get no item, so
 //           they launch no MFMA work)
 //   scatter one block per chunk: the chunk is walked in order; inside a wave
 //           equal experts are found with nine ballots (expert id bits plus a
@@ -15,7 +15,8 @@
 //           therefore increasing (t, k).
 //
 // The host never reads the counts: the GEMM grids are sized by the bound
-// ceil(T*K / bm) + E on the number of tiles and surplus blocks exit.
+// (ceil(T*K / bm) + E) * column tiles on the number of items and surplus
+// blocks exit.
 #include "moe_common.h"
 
 namespace moe {
@@ -54,11 +55,20 @@ __device__ int block_exclusive_scan(int* v, int* tmp, int n) {
   return total;
 }
 
+// Position of work item b in the operand-sharing order: blocks are handed to
+// the 8 XCDs round-robin (b % 8), so XCD x receives one contiguous range of
+// the order and its concurrently running tiles share expert rows and weight
+// column tiles in its L2.  A bijection of [0, total).
+__device__ __forceinline__ int xcd_order(int b, int total) {
+  const int q = total / 8, r = total % 8, x = b % 8, i = b / 8;
+  return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(DispatchArgs a) {
   __shared__ int part[kScanThreads];   // [J][E] partial chunk sums, then their prefixes
   __shared__ int tmp[kScanThreads];
-  __shared__ int offs[kMaxExperts];
-  __shared__ int tstart[kMaxExperts];
+  __shared__ int offs[kMaxExperts + 1];
+  __shared__ int tst[kMaxExperts + 1];
   __shared__ int cnts[kMaxExperts];
   const int tid = threadIdx.x;
   const int E = a.E;
@@ -80,23 +90,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DispatchArgs a) {
       part[jj * E + tid] = run;
       run += v;
     }
-    offs[tid] = run;                                    // count, scanned below
-    tstart[tid] = (run + a.bm - 1) / a.bm;              // tiles, scanned below
+    offs[tid] = run;  // count, scanned below
     cnts[tid] = run;
     a.counts[tid] = run;
     if (a.counts_out) a.counts_out[tid] = run;
   }
   __syncthreads();
   const int M = block_exclusive_scan(offs, tmp, E);
-  const int ntiles = block_exclusive_scan(tstart, tmp, E);
-  if (tid < E) {
+  if (tid == 0) offs[E] = M;
+  if (tid <= E) {
     a.offsets[tid] = offs[tid];
     if (a.offsets_out) a.offsets_out[tid] = offs[tid];
-  }
-  if (tid == 0) {
-    a.offsets[E] = M;
-    if (a.offsets_out) a.offsets_out[E] = M;
-    a.num_tiles[0] = ntiles;
   }
   if (worker) {
     int base = offs[e] + part[j * E + e];
@@ -106,14 +110,46 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DispatchArgs a) {
       a.chunk_base[idx] = base;
       base += c;
     }
-    const int cnt = cnts[e];
-    const int nt = (cnt + a.bm - 1) / a.bm;
-    for (int t = j; t < nt; t += J) {
-      const int slot = tstart[e] + t;
-      if (slot < a.max_tiles) {
-        a.tile_e[slot] = e;
-        a.tile_r0[slot] = offs[e] + t * a.bm;
+  }
+
+  // Work lists of the grouped GEMMs.  Order: experts ascending; inside an
+  // expert, groups of kColGroup column tiles; inside a group, column tile
+  // slowest and row tile fastest.  Empty experts contribute no item.
+  for (int g = 0; g < a.nspec; ++g) {
+    const WorkSpec& sp = a.spec[g];
+    __syncthreads();
+    if (tid < E) tst[tid] = (cnts[tid] + sp.bm - 1) / sp.bm;
+    __syncthreads();
+    const int tiles = block_exclusive_scan(tst, tmp, E);
+    if (tid == 0) tst[E] = tiles;
+    __syncthreads();
+    const int ntn = sp.ntn;
+    const int total = tiles * ntn;
+    if (tid == 0) sp.num_work[0] = total;
+    for (int b = tid; b < total && b < sp.max_work; b += kScanThreads) {
+      const int L = xcd_order(b, total);
+      // expert: the last x with tst[x] * ntn <= L
+      int lo = 0, hi = E;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tst[mid] * ntn <= L) lo = mid; else hi = mid;
       }
+      const int x = lo;
+      const int mt = tst[x + 1] - tst[x];
+      const int q = L - tst[x] * ntn;
+      const int full = (ntn / kColGroup) * kColGroup * mt;
+      int m, n;
+      if (q < full) {
+        const int gsz = kColGroup * mt;
+        const int grp = q / gsz, r = q - grp * gsz;
+        n = grp * kColGroup + r / mt;
+        m = r % mt;
+      } else {
+        const int r = q - full;
+        n = (ntn / kColGroup) * kColGroup + r / mt;
+        m = r % mt;
+      }
+      sp.work[b] = make_int2(x | (n << 8), offs[x] + m * sp.bm);
     }
   }
 }

@@ -12,9 +12,10 @@
 //                     "Weight the selected outputs"), either with fp32 atomics
 //                     or into the row's own (t,k) slot for an ordered sum.
 //
-// Rows r are assignments in expert-contiguous order; tile j of the tile table
-// covers up to kGemmBM rows of one expert.  x rows are gathered through the
-// sorted token ids while they are loaded, so no permuted copy of x exists.
+// Rows r are assignments in expert-contiguous order; a work item covers up to
+// 128 rows of one expert and 128 output columns (this generic variant).  x
+// rows are gathered through the sorted token ids while they are loaded, so no
+// permuted copy of x exists.
 // Every contraction accumulates in fp32 and the gate_up result is rounded
 // once to the compute dtype (Dew "Mixture of experts" page, section "Expert
 // computation and placement").
@@ -27,6 +28,7 @@
 // consume the current one.  Weights are MFMA operand 0 and activations operand
 // 1, so each lane's four accumulators are four consecutive output columns of
 // one row.
+#include "gemm_epilogue.h"
 #include "moe_common.h"
 
 namespace moe {
@@ -73,12 +75,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   __shared__ uint4 As[BM * 8];
   __shared__ uint4 Bs[NB * 8];
 
-  const int j = blockIdx.x;
-  if (j >= a.num_tiles[0]) return;
-  const int e = a.tile_e[j];
-  const int r0 = a.tile_r0[j];
+  if ((int)blockIdx.x >= a.num_work[0]) return;
+  const int2 wk = a.work[blockIdx.x];
+  const int e = wk.x & 0xff;
+  const int r0 = wk.y;
   const int rows = min(BM, a.offsets[e + 1] - r0);
-  const int64_t n0 = (int64_t)blockIdx.y * BN;
+  const int64_t n0 = (int64_t)(wk.x >> 8) * BN;
   const int64_t N = a.N, Kd = a.Kd;
   const bool vec = a.vec_ok != 0;
 
@@ -196,84 +198,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   for (int mi = 0; mi < SM; ++mi) {
     const int m = wm * WTM + mi * 16 + l16;
     if (m >= rows) continue;
-    const int r = r0 + m;
-    float wgt = 1.f;
-    int64_t orow = r;
-    if constexpr (EPI == EPI_DOWN_ATOMIC || EPI == EPI_DOWN_SLOT) {
-      wgt = a.sorted_w[r];
-      orow = (EPI == EPI_DOWN_ATOMIC) ? (int64_t)a.sorted_tok[r] : (int64_t)a.sorted_slot[r];
-    }
+    const RowCtx rc = row_ctx<EPI>(a, r0 + m);
 #pragma unroll
-    for (int ni = 0; ni < SN; ++ni) {
-      const int64_t nb = n0 + wn * WTN + ni * 16 + 4 * g;
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t n = nb + i;
-        const bool ok = n < N;
-        if constexpr (EPI == EPI_SWIGLU) {
-          float gg = acc[0][mi][ni][i], uu = acc[1][mi][ni][i];
-          if (bias && ok) {
-            gg += bias[n];
-            uu += bias[a.up_off + n];
-          }
-          v[i] = gg / (1.f + __expf(-gg)) * uu;
-        } else if constexpr (EPI == EPI_RELU) {
-          float t = acc[0][mi][ni][i];
-          if (bias && ok) t += bias[n];
-          v[i] = fmaxf(t, 0.f);
-        } else {
-          float t = acc[0][mi][ni][i];
-          if (bias && ok) t += bias[n];
-          v[i] = wgt * t;
-        }
-      }
-      if constexpr (EPI == EPI_DOWN_ATOMIC) {
-        float* dst = static_cast<float*>(a.C) + orow * a.ldc;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (nb + i < N) unsafeAtomicAdd(dst + nb + i, v[i]);
-      } else if constexpr (EPI == EPI_DOWN_SLOT) {
-        float* dst = static_cast<float*>(a.C) + orow * a.ldc + nb;
-        if (nb + 4 <= N && (a.ldc & 3) == 0) {
-          *reinterpret_cast<float4*>(dst) = float4{v[0], v[1], v[2], v[3]};
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (nb + i < N) dst[i] = v[i];
-        }
-      } else {
-        elem* dst = static_cast<elem*>(a.C) + orow * a.ldc + nb;
-        if constexpr (EPC == 8) {
-          if (nb + 4 <= N && (a.ldc & 3) == 0) {
-            uint2 pk;
-            pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-            pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-            *reinterpret_cast<uint2*>(dst) = pk;
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (nb + i < N) dst[i] = (uint16_t)f32_to_bf16_bits(v[i]);
-          }
-        } else {
-          if (nb + 4 <= N && (a.ldc & 3) == 0) {
-            *reinterpret_cast<float4*>(dst) = float4{v[0], v[1], v[2], v[3]};
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (nb + i < N) dst[i] = v[i];
-          }
-        }
-      }
-    }
+    for (int ni = 0; ni < SN; ++ni)
+      epilogue4<elem, EPI>(a, rc, n0 + wn * WTN + ni * 16 + 4 * g, acc[0][mi][ni], acc[NACC - 1][mi][ni], bias);
   }
 }
 
 template <typename Tag, int EPI>
 hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
-  constexpr int BM = kGemmBM, BN = 128;
-  const unsigned gy = (unsigned)((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((grouped_gemm_kernel<Tag, EPI, BM, BN>), dim3(a.max_tiles, gy), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<Tag, EPI, 128, 128>), dim3(a.max_work), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -302,8 +236,22 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
 
 }  // namespace
 
-hipError_t launch_grouped_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
-  if (a.max_tiles <= 0 || a.N <= 0) return hipSuccess;
+int variant_rows(int var) {
+  switch (var) {
+    case VAR_BF16_M256: return 256;
+    case VAR_BF16_M32: return 32;
+    default: return 128;
+  }
+}
+
+int variant_cols(int var, bool dual) {
+  if (var == VAR_GENERIC) return 128;
+  return dual ? 128 : 256;
+}
+
+hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s) {
+  if (a.max_work <= 0 || a.N <= 0) return hipSuccess;
+  if (var != VAR_GENERIC) return launch_gemm_bf16(epi, var, a, s);
   return dtype == 1 ? launch_tag<BF16>(epi, a, s) : launch_tag<F32>(epi, a, s);
 }
 

@@ -17,11 +17,18 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// One grouped GEMM's plan: kernel variant and work-list geometry.
+struct GemmPlan {
+  int var = VAR_GENERIC;
+  int32_t bm = 128, cols = 128, ntn = 0, max_work = 0;
+};
+
 struct Layout {
   int64_t M = 0;
-  int32_t nchunks = 0, max_tiles = 0;
-  size_t sel32 = 0, chunk_counts = 0, chunk_base = 0, counts = 0, offsets = 0, tile_e = 0, tile_r0 = 0,
-         num_tiles = 0, sorted_tok = 0, sorted_slot = 0, sorted_w = 0, logits = 0, h = 0, slots = 0, acc = 0,
+  int32_t nchunks = 0;
+  GemmPlan g1, g2;
+  size_t sel32 = 0, chunk_counts = 0, chunk_base = 0, counts = 0, offsets = 0, work1 = 0, work2 = 0,
+         num_work = 0, sorted_tok = 0, sorted_slot = 0, sorted_w = 0, logits = 0, h = 0, slots = 0, acc = 0,
          total = 0;
 };
 
@@ -36,19 +43,45 @@ moe_status check_desc(const moe_desc* d) {
   if (d->E < 1 || d->E > MOE_MAX_EXPERTS || d->K < 1 || d->K > d->E) return MOE_EINVAL;
   if (d->D > INT_MAX || d->F > INT_MAX) return MOE_EINVAL;
   if (d->T > (int64_t)INT_MAX / d->K) return MOE_EINVAL;  // row ids are int32
+  // work-list sizes stay within int32 (checked at the smallest tile shape)
+  const int64_t M = d->T * d->K;
+  const int64_t tiles = M / 32 + d->E + 1;
+  const int64_t cols = d->F / 128 + d->D / 128 + 2;
+  if (tiles * cols > (int64_t)INT_MAX) return MOE_EINVAL;
   return MOE_OK;
+}
+
+// Variant for one GEMM: the bf16 direct-to-LDS kernel when K is a multiple of
+// 64 and byte offsets fit in 32 bits; its row tile follows the mean number of
+// rows per expert (decode-sized segments get 32-row tiles).
+GemmPlan plan_gemm(const moe_desc* d, int64_t M, int64_t N, int64_t Kd, int64_t a_rows, int64_t b_expert_elems,
+                   bool dual) {
+  GemmPlan p;
+  const bool bf16_ok = d->dtype == MOE_BF16 && Kd % 64 == 0 && a_rows * Kd * 2 < (int64_t)UINT32_MAX &&
+                       b_expert_elems * 2 < (int64_t)UINT32_MAX;
+  if (bf16_ok) {
+    const int64_t mean = M / d->E;
+    p.var = mean >= 512 ? VAR_BF16_M256 : (mean >= 64 ? VAR_BF16_M128 : VAR_BF16_M32);
+  }
+  p.bm = variant_rows(p.var);
+  p.cols = variant_cols(p.var, dual);
+  p.ntn = (int32_t)((N + p.cols - 1) / p.cols);
+  const int64_t bound = (M + p.bm - 1) / p.bm + d->E;
+  const int64_t tiles = M < bound ? M : bound;
+  p.max_work = (int32_t)(tiles * p.ntn);
+  return p;
 }
 
 Layout layout_of(const moe_desc* d) {
   Layout L;
   const int64_t T = d->T, D = d->D, F = d->F, E = d->E, K = d->K;
   const int64_t M = T * K;
-  const int64_t G = d->act == MOE_ACT_SWIGLU ? 2 : 1;
-  (void)G;
+  const bool swiglu = d->act == MOE_ACT_SWIGLU;
+  const int64_t G = swiglu ? 2 : 1;
   L.M = M;
   L.nchunks = (int32_t)((M + kDispatchChunk - 1) / kDispatchChunk);
-  const int64_t bound = (M + kGemmBM - 1) / kGemmBM + E;
-  L.max_tiles = (int32_t)(M < bound ? M : bound);
+  L.g1 = plan_gemm(d, M, F, D, T, G * F * D, swiglu);
+  L.g2 = plan_gemm(d, M, D, F, M, D * F, false);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -60,9 +93,9 @@ Layout layout_of(const moe_desc* d) {
   L.chunk_base = take(sizeof(int32_t) * (size_t)L.nchunks * E);
   L.counts = take(sizeof(int32_t) * E);
   L.offsets = take(sizeof(int32_t) * (E + 1));
-  L.tile_e = take(sizeof(int32_t) * (size_t)L.max_tiles);
-  L.tile_r0 = take(sizeof(int32_t) * (size_t)L.max_tiles);
-  L.num_tiles = take(sizeof(int32_t));
+  L.work1 = take(sizeof(int2) * (size_t)L.g1.max_work);
+  L.work2 = take(sizeof(int2) * (size_t)L.g2.max_work);
+  L.num_work = take(sizeof(int32_t) * 2);
   L.sorted_tok = take(sizeof(int32_t) * M);
   L.sorted_slot = take(sizeof(int32_t) * M);
   L.sorted_w = take(sizeof(float) * M);
@@ -95,7 +128,7 @@ struct Marks {
 moe_status route_and_sort(const moe_desc* d, const Layout& L, const void* x, const void* router,
                           const float* router_bias, int64_t* sel, float* weights, float* logits,
                           int32_t* counts_out, int32_t* offsets_out, int32_t* sorted_tok, int32_t* sorted_slot,
-                          float* zero_rows, void* ws, hipStream_t s, const Marks& mk) {
+                          float* zero_rows, void* ws, hipStream_t s, const Marks& mk, bool build_work) {
   const int eb = elem_bytes(d->dtype);
   RouterArgs ra{};
   ra.x = x;
@@ -131,11 +164,16 @@ moe_status route_and_sort(const moe_desc* d, const Layout& L, const void* x, con
   da.sorted_tok = sorted_tok ? sorted_tok : at<int32_t>(ws, L.sorted_tok);
   da.sorted_slot = sorted_slot ? sorted_slot : at<int32_t>(ws, L.sorted_slot);
   da.sorted_w = at<float>(ws, L.sorted_w);
-  da.bm = kGemmBM;
-  da.max_tiles = L.max_tiles;
-  da.tile_e = at<int32_t>(ws, L.tile_e);
-  da.tile_r0 = at<int32_t>(ws, L.tile_r0);
-  da.num_tiles = at<int32_t>(ws, L.num_tiles);
+  da.nspec = build_work ? 2 : 0;
+  const GemmPlan* plans[2] = {&L.g1, &L.g2};
+  const size_t works[2] = {L.work1, L.work2};
+  for (int i = 0; i < 2; ++i) {
+    da.spec[i].bm = plans[i]->bm;
+    da.spec[i].ntn = plans[i]->ntn;
+    da.spec[i].max_work = plans[i]->max_work;
+    da.spec[i].work = at<int2>(ws, works[i]);
+    da.spec[i].num_work = at<int32_t>(ws, L.num_work) + i;
+  }
   if (launch_dispatch(da, s) != hipSuccess || !mk.mark(2)) return MOE_EDEVICE;
   return MOE_OK;
 }
@@ -164,7 +202,7 @@ moe_status forward_impl(const moe_desc* d, const void* x, const void* router, co
 
   if (!mk.mark(0)) return MOE_EDEVICE;
   st = route_and_sort(d, L, x, router, router_bias, selected_experts, routing_weights, router_logits, expert_counts,
-                      nullptr, nullptr, nullptr, acc, workspace, s, mk);
+                      nullptr, nullptr, nullptr, acc, workspace, s, mk, true);
   if (st != MOE_OK) return st;
 
   GemmArgs g{};
@@ -177,11 +215,10 @@ moe_status forward_impl(const moe_desc* d, const void* x, const void* router, co
   g.up_off = d->F;
   g.N = d->F;
   g.Kd = d->D;
-  g.tile_e = at<int32_t>(workspace, L.tile_e);
-  g.tile_r0 = at<int32_t>(workspace, L.tile_r0);
-  g.num_tiles = at<int32_t>(workspace, L.num_tiles);
+  g.work = at<int2>(workspace, L.work1);
+  g.num_work = at<int32_t>(workspace, L.num_work);
+  g.max_work = L.g1.max_work;
   g.offsets = at<int32_t>(workspace, L.offsets);
-  g.max_tiles = L.max_tiles;
   g.bias = up_bias;
   g.bias_estride = G * d->F;
   g.C = at<void>(workspace, L.h);
@@ -190,7 +227,8 @@ moe_status forward_impl(const moe_desc* d, const void* x, const void* router, co
   g.sorted_slot = at<int32_t>(workspace, L.sorted_slot);
   g.sorted_w = at<float>(workspace, L.sorted_w);
   g.vec_ok = aligned16(x) && aligned16(gate_up_proj) && ((d->D * eb) % 16 == 0);
-  if (launch_grouped_gemm(d->dtype, swiglu ? EPI_SWIGLU : EPI_RELU, g, s) != hipSuccess || !mk.mark(3))
+  if (launch_grouped_gemm(d->dtype, swiglu ? EPI_SWIGLU : EPI_RELU, L.g1.var, g, s) != hipSuccess ||
+      !mk.mark(3))
     return MOE_EDEVICE;
 
   GemmArgs h = g;
@@ -207,8 +245,12 @@ moe_status forward_impl(const moe_desc* d, const void* x, const void* router, co
   h.bias_estride = d->D;
   h.C = d->deterministic ? at<void>(workspace, L.slots) : static_cast<void*>(acc);
   h.ldc = d->D;
+  h.work = at<int2>(workspace, L.work2);
+  h.num_work = at<int32_t>(workspace, L.num_work) + 1;
+  h.max_work = L.g2.max_work;
   h.vec_ok = aligned16(down_proj) && ((d->F * eb) % 16 == 0);
-  if (launch_grouped_gemm(d->dtype, d->deterministic ? EPI_DOWN_SLOT : EPI_DOWN_ATOMIC, h, s) != hipSuccess ||
+  if (launch_grouped_gemm(d->dtype, d->deterministic ? EPI_DOWN_SLOT : EPI_DOWN_ATOMIC, L.g2.var, h, s) !=
+          hipSuccess ||
       !mk.mark(4))
     return MOE_EDEVICE;
 
@@ -287,7 +329,7 @@ moe_status moe_dispatch(const moe_desc* d, const void* x, const void* router, co
   const Marks none{nullptr, 0, nullptr};
   return route_and_sort(d, L, x, router, router_bias, selected_experts, routing_weights, router_logits,
                         expert_counts, expert_offsets, sorted_token, sorted_slot, nullptr, workspace,
-                        static_cast<hipStream_t>(stream), none);
+                        static_cast<hipStream_t>(stream), none, false);
 }
 
 }  // extern "C"

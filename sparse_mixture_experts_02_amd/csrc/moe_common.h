@@ -39,7 +39,6 @@ __device__ __forceinline__ float to_f32(uint16_t v) { return bf16_bits_to_f32(v)
 constexpr int kMaxExperts = 256;
 constexpr int kRouterTokens = 16;     // tokens per router block
 constexpr int kDispatchChunk = 1024;  // assignments per count/scatter block
-constexpr int kGemmBM = 128;          // rows (tokens) per grouped-GEMM tile
 
 // ------------------------------------------------------------ launchers
 struct RouterArgs {
@@ -58,6 +57,20 @@ struct RouterArgs {
 };
 hipError_t launch_router(int dtype, const RouterArgs& a, hipStream_t s);
 
+// A grouped GEMM's work list: item b is one (expert, row tile, column tile).
+// Items are ordered so that consecutive items share operands (all row tiles of
+// one expert over a group of column tiles) and are laid out so that the items
+// one XCD runs (blocks b with b % 8 == xcd) form one contiguous range of that
+// order; the GEMM grid is sized by max_work and blocks b >= *num_work exit.
+struct WorkSpec {
+  int32_t bm;        // rows per tile
+  int32_t ntn;       // column tiles
+  int32_t max_work;  // upper bound of the item count (grid size)
+  int2* work;        // (max_work) {expert | column_tile << 8, first sorted row}
+  int32_t* num_work; // (1)
+};
+constexpr int kColGroup = 4;  // column tiles per ordering group
+
 struct DispatchArgs {
   const int32_t* sel32;   // (M) expert of assignment i = t*K + k
   const float* weights;   // (M)
@@ -73,17 +86,22 @@ struct DispatchArgs {
   int32_t* sorted_tok;    // (M)
   int32_t* sorted_slot;   // (M)
   float* sorted_w;        // (M) or null
-  // tile table for the grouped GEMMs: tile j covers rows [tile_r0[j],
-  // min(tile_r0[j] + bm, offsets[tile_e[j]+1])) of expert tile_e[j].
-  int32_t bm;
-  int32_t max_tiles;
-  int32_t* tile_e;
-  int32_t* tile_r0;
-  int32_t* num_tiles;     // (1)
+  int32_t nspec;          // work lists to build (0..2)
+  WorkSpec spec[2];
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 
 enum Epilogue { EPI_SWIGLU = 0, EPI_RELU = 1, EPI_DOWN_ATOMIC = 2, EPI_DOWN_SLOT = 3 };
+
+// Kernel variants of the grouped GEMM.
+//   GENERIC: any K / alignment, fp32 or bf16; 128x128 output tiles, operands
+//            staged through registers into LDS.
+//   BF16_Mxxx: bf16 with K a multiple of 64 and 16-byte aligned rows; LDS
+//            double buffer filled by direct global->LDS loads; xxx rows per
+//            tile (256 and 128 for prefill, 32 for decode-sized segments).
+enum Variant { VAR_GENERIC = 0, VAR_BF16_M256 = 1, VAR_BF16_M128 = 2, VAR_BF16_M32 = 3 };
+int variant_rows(int var);
+int variant_cols(int var, bool dual);
 
 struct GemmArgs {
   const void* A;            // activation rows
@@ -95,11 +113,10 @@ struct GemmArgs {
   int64_t up_off;           // rows between gate and up halves (SwiGLU)
   int64_t N;                // output columns
   int64_t Kd;               // contraction length
-  const int32_t* tile_e;
-  const int32_t* tile_r0;
-  const int32_t* num_tiles;
+  const int2* work;
+  const int32_t* num_work;
+  int32_t max_work;
   const int32_t* offsets;
-  int32_t max_tiles;
   const float* bias;        // per-expert bias rows or null
   int64_t bias_estride;
   void* C;                  // h (G1) / out accumulation (G2 atomic) / slot rows (G2 slot)
@@ -109,7 +126,8 @@ struct GemmArgs {
   const float* sorted_w;
   int32_t vec_ok;           // rows 16-byte aligned: vector loads allowed
 };
-hipError_t launch_grouped_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s);
+hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_bf16(int epi, int var, const GemmArgs& a, hipStream_t s);
 
 struct FinalizeArgs {
   const float* src;   // slot rows (T*K, D) when K > 0 slots, or (T, D) accumulation

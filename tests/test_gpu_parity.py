@@ -83,6 +83,14 @@ EDGE = [
     (129, 256, 96, 256, 4, "swiglu", "bf16", False, True),
     (2048, 256, 512, 16, 4, "relu", "bf16", True, True),
     (77, 8, 8, 37, 37, "swiglu", "f32", False, True),
+    # bf16 shapes on the direct-to-LDS kernels (K a multiple of 64), with
+    # ragged row tiles and column tails: 128-row, 256-row and 32-row tiles
+    (1000, 128, 320, 4, 2, "swiglu", "bf16", False, True),
+    (600, 192, 448, 3, 1, "relu", "bf16", True, True),
+    (4096, 128, 192, 4, 2, "swiglu", "bf16", False, True),
+    (40, 256, 384, 8, 2, "swiglu", "bf16", False, True),
+    (64, 4096, 1024, 8, 2, "swiglu", "bf16", False, True),
+    (3000, 64, 128, 40, 6, "swiglu", "bf16", False, True),
 ]
 
 
