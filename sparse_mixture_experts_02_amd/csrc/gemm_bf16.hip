@@ -127,27 +127,33 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) co[s] = ((s * 4 + g) ^ (l16 & 7)) * 16;
 
+  // One K step from one LDS stage: two sub-steps of 32 k.  Per sub-step the
+  // B fragments are read first; the A fragments are read two MFMA groups
+  // ahead of their use (group mi = the NACC*SN MFMAs of A fragment mi), and
+  // scheduling barriers keep that order, so every A read has a whole group of
+  // MFMAs in flight to return behind.
   auto compute = [&](const char* buf) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       bf16x8 fa[SM], fb[NACC][SN];
 #pragma unroll
-      for (int mi = 0; mi < SM; ++mi)
-        fa[mi] = *reinterpret_cast<const bf16x8*>(buf + (arow + mi * 16) * 128 + co[s]);
-#pragma unroll
       for (int q = 0; q < NACC; ++q)
 #pragma unroll
         for (int ni = 0; ni < SN; ++ni)
           fb[q][ni] = *reinterpret_cast<const bf16x8*>(buf + AB + (q * OUTC + brow + ni * 16) * 128 + co[s]);
+      fa[0] = *reinterpret_cast<const bf16x8*>(buf + arow * 128 + co[s]);
+      if (SM > 1) fa[1] = *reinterpret_cast<const bf16x8*>(buf + (arow + 16) * 128 + co[s]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < NACC; ++q)
+      for (int mi = 0; mi < SM; ++mi) {
+        if (mi + 2 < SM) fa[mi + 2] = *reinterpret_cast<const bf16x8*>(buf + (arow + (mi + 2) * 16) * 128 + co[s]);
 #pragma unroll
-        for (int mi = 0; mi < SM; ++mi)
+        for (int q = 0; q < NACC; ++q)
 #pragma unroll
           for (int ni = 0; ni < SN; ++ni)
             acc[q][mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[q][ni], fa[mi], acc[q][mi][ni], 0, 0, 0);
-      // keep one K sub-step's fragments live at a time
-      __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
