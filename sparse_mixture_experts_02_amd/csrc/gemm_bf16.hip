@@ -127,33 +127,48 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) co[s] = ((s * 4 + g) ^ (l16 & 7)) * 16;
 
-  // One K step from one LDS stage: two sub-steps of 32 k.  Per sub-step the
-  // B fragments are read first; the A fragments are read two MFMA groups
-  // ahead of their use (group mi = the NACC*SN MFMAs of A fragment mi), and
-  // scheduling barriers keep that order, so every A read has a whole group of
-  // MFMAs in flight to return behind.
+  // One K step from one LDS stage: two sub-steps of 32 k.  A "group" is the
+  // NACC*SN MFMAs of one A fragment.  Reads are spread over the groups so that
+  // each one is issued a whole group before its use: the A fragments two
+  // groups ahead, the second sub-step's B fragments one per group of the first
+  // sub-step, and its first two A fragments during the last two groups.  Only
+  // the first sub-step's B fragments and first A fragments wait on LDS, once
+  // per stage.  Scheduling barriers keep that order.
+  constexpr int NB = NACC * SN;
+  auto rdA = [&](const char* buf, int s, int mi) {
+    return *reinterpret_cast<const bf16x8*>(buf + (arow + mi * 16) * 128 + co[s]);
+  };
+  auto rdB = [&](const char* buf, int s, int j) {
+    return *reinterpret_cast<const bf16x8*>(buf + AB + ((j / SN) * OUTC + brow + (j % SN) * 16) * 128 + co[s]);
+  };
   auto compute = [&](const char* buf) {
+    bf16x8 fa0[SM], fa1[SM], fb0[NB], fb1[NB];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 fa[SM], fb[NACC][SN];
+    for (int j = 0; j < NB; ++j) fb0[j] = rdB(buf, 0, j);
+    fa0[0] = rdA(buf, 0, 0);
+    if (SM > 1) fa0[1] = rdA(buf, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < NACC; ++q)
+    for (int mi = 0; mi < SM; ++mi) {
+      if (mi + 2 < SM) fa0[mi + 2] = rdA(buf, 0, mi + 2);
+      if (mi + 2 == SM) fa1[0] = rdA(buf, 1, 0);
+      if (mi + 1 == SM && SM > 1) fa1[1] = rdA(buf, 1, 1);
 #pragma unroll
-        for (int ni = 0; ni < SN; ++ni)
-          fb[q][ni] = *reinterpret_cast<const bf16x8*>(buf + AB + (q * OUTC + brow + ni * 16) * 128 + co[s]);
-      fa[0] = *reinterpret_cast<const bf16x8*>(buf + arow * 128 + co[s]);
-      if (SM > 1) fa[1] = *reinterpret_cast<const bf16x8*>(buf + (arow + 16) * 128 + co[s]);
+      for (int j = mi * NB / SM; j < (mi + 1) * NB / SM; ++j) fb1[j] = rdB(buf, 1, j);
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        acc[j / SN][mi][j % SN] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb0[j], fa0[mi], acc[j / SN][mi][j % SN], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-      for (int mi = 0; mi < SM; ++mi) {
-        if (mi + 2 < SM) fa[mi + 2] = *reinterpret_cast<const bf16x8*>(buf + (arow + (mi + 2) * 16) * 128 + co[s]);
+    for (int mi = 0; mi < SM; ++mi) {
+      if (mi + 2 < SM) fa1[mi + 2] = rdA(buf, 1, mi + 2);
 #pragma unroll
-        for (int q = 0; q < NACC; ++q)
-#pragma unroll
-          for (int ni = 0; ni < SN; ++ni)
-            acc[q][mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[q][ni], fa[mi], acc[q][mi][ni], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int j = 0; j < NB; ++j)
+        acc[j / SN][mi][j % SN] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb1[j], fa1[mi], acc[j / SN][mi][j % SN], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -165,6 +180,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
     if (kt + 1 < nk) issue(kt + 1, lds + ((kt + 1) & 1) * STAGE);
     compute(lds + (kt & 1) * STAGE);
   }
+  wait_vm0();  // no LDS DMA may outlive the workgroup
 
   const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;
 #pragma unroll
