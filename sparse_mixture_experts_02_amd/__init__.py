@@ -185,13 +185,15 @@ def _prepare(x, router, gate_up_proj, down_proj, top_k, act):
 
 
 def forward(x, router, gate_up_proj, down_proj, *, top_k, norm_topk_prob=True, act="silu", router_bias=None,
-            up_bias=None, down_bias=None, out_dtype=None, deterministic=False, return_logits=False,
+            up_bias=None, down_bias=None, out_dtype=None, deterministic=True, return_logits=False,
             return_counts=False, workspace=None):
     """Layer forward on the device of x.
 
     Returns (out with the shape of x, selected_experts int64 (T,K),
     routing_weights fp32 (T,K)) plus router_logits (T,E) and expert_counts (E)
-    when requested.  ``out_dtype`` defaults to float32.
+    when requested.  ``out_dtype`` defaults to float32.  ``deterministic``
+    (default) sums each token's K expert rows in k order; False adds them with
+    fp32 atomics instead.
     """
     torch = _torch()
     D, F, E = _prepare(x, router, gate_up_proj, down_proj, top_k, act)

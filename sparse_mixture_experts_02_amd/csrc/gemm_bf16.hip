@@ -4,22 +4,21 @@
 // rounding of h to bf16).
 //
 // Tile: BM sorted rows x 256 weight rows (SwiGLU: 128 gate + the 128 matching
-// up rows, so 128 h columns; otherwise 256 output columns), K step 64.
-// 4 waves: 2 x 2 for BM = 256 / 128 (a wave owns BM/2 rows x 128 weight rows),
-// 1 x 4 for BM = 32 (32 rows x 64 weight rows).  MFMA v_mfma_f32_16x16x32_bf16
-// with the weights as operand 0, so a lane's accumulators are four
-// consecutive output columns of one row.
+// up rows, so 128 h columns; otherwise 256 output columns).  MFMA
+// v_mfma_f32_32x32x16_bf16 with the weights as operand 0, so a lane's
+// accumulators are groups of four consecutive output columns of one row.
+// Prefill tiles (BM 256/128) run 8 waves, two per SIMD, 2 x 4 over the tile;
+// the decode tile (BM 32) runs 4 waves side by side along the weight rows.
 //
 // Data path: global_load_lds_dwordx4 writes each 16-byte chunk straight from
-// HBM/L2 into LDS (no staging registers), into two LDS stages held in two
-// distinct arrays so the compiler sees that the loads in flight into one stage
-// do not alias the MFMA fragment reads from the other.  Rows are 128 bytes in
-// LDS with the 16-byte chunk index XOR-ed with (row & 7): a wave's fragment
-// read of 16 rows at one chunk spreads over all banks.  A lane of a load
-// instruction writes LDS byte 16*lane of an 8-row block, so it loads the
-// global chunk that the swizzle puts there.  One barrier per K step: waves
-// wait for their own loads (vmcnt 0), then the barrier publishes the stage and
-// frees the other one for the next loads.
+// HBM/L2 into LDS (no staging registers).  LDS holds S stages of KB bytes of
+// K per row; rows are KB bytes with the 16-byte chunk index XOR-ed with the
+// low row bits, so a wave's fragment read of 32 rows at one chunk spreads over
+// the banks.  A lane of a load instruction writes LDS byte 16*lane of a
+// block of 1024/KB rows, so it loads the global chunk the swizzle puts there.
+// The loads of a stage are issued S-1 steps before it is consumed; one
+// barrier per step, waited on only for the loads of the stage being
+// published (s_waitcnt vmcnt with the later stages left in flight).
 //
 // Requires K % 64 == 0, 16-byte aligned operands, and operand regions under
 // 4 GiB (32-bit byte offsets); the host routes anything else to the generic
@@ -30,35 +29,67 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-
 // One 16-byte chunk from global memory straight into LDS: lane l of the wave
 // writes LDS bytes [dst + 16*l, dst + 16*l + 16); dst must be wave-uniform.
 __device__ __forceinline__ void lds_dma16(const char* src, char* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
-__device__ __forceinline__ void wait_vm0() {
-  // s_waitcnt vmcnt(0); expcnt and lgkmcnt left unconstrained (gfx9 encoding).
-  __builtin_amdgcn_s_waitcnt(0x0f70);
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left unconstrained (gfx9
+// encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
 }
 
-template <int EPI, int BM>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
+// Workgroup barrier for LDS.  The stage data arrives by LDS DMA, whose
+// completion each wave has awaited with wait_vm; __syncthreads would also
+// drain the loads still in flight for later stages.  The memory clobber keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
+
+// Waves per block for a row-tile size.  Prefill tiles run 8 waves (two per
+// SIMD): while one wave waits on a barrier, an LDS read or a load issue, the
+// other keeps the matrix core busy.  The decode tile runs 4.
+// Kernel shape: BM rows per tile, NW waves (M of them along the rows), KB
+// bytes of K per LDS stage, S stages.
+template <int BM_, int NW_, int M_, int KB_, int S_>
+struct Shape {
+  static constexpr int BM = BM_, NW = NW_, M = M_, KB = KB_, S = S_;
+};
+// Chosen by a sweep on the Mixtral-shaped layer (MI355X): for the prefill
+// tiles two 64 KB stages with 8 waves beat deeper pipelines of 32 KB stages
+// (which need twice the barriers); the decode tile is a weight stream and
+// wants more bytes in flight.
+using ShapeM256 = Shape<256, 8, 2, 128, 2>;  // 2 x 64 KB of LDS
+using ShapeM128 = Shape<128, 4, 2, 128, 2>;  // 2 x 48 KB
+using ShapeM32 = Shape<32, 4, 1, 128, 4>;    // 4 x 36 KB
+
+template <int EPI, class SH>
+__global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int BM = SH::BM;
   constexpr bool DUAL = EPI == EPI_SWIGLU;
-  constexpr int WAVES_M = BM >= 128 ? 2 : 1;
-  constexpr int WAVES_N = 4 / WAVES_M;
-  constexpr int WM = BM / WAVES_M, SM = WM / 16;
+  constexpr int NW = SH::NW;
+  constexpr int WAVES_M = SH::M;
+  constexpr int KB = SH::KB, S = SH::S;
+  constexpr int CPR = KB / 16;      // 16-byte chunks per LDS row
+  constexpr int RPI = 1024 / KB;    // rows per load instruction
+  constexpr int NT = KB / 32;       // 16-k MFMA slices per stage
+  constexpr int WAVES_N = NW / WAVES_M;
+  constexpr int WM = BM / WAVES_M, SM = WM / 32;  // 32-row MFMA tiles per wave
   constexpr int NBR = 256;                      // weight rows per tile
   constexpr int OUTC = DUAL ? 128 : 256;        // output columns per tile
-  constexpr int WN = OUTC / WAVES_N, SN = WN / 16;
+  constexpr int WN = OUTC / WAVES_N, SN = WN / 32;  // 32-column MFMA tiles per wave (per half)
   constexpr int NACC = DUAL ? 2 : 1;
-  constexpr int AB = BM * 128;                  // A bytes per stage
-  constexpr int STAGE = AB + NBR * 128;
-  constexpr int AI = BM / 32;                   // A load instructions per wave
-  constexpr int BI = NBR / 32;                  // B load instructions per wave
+  constexpr int AB = BM * KB;                   // A bytes per stage
+  constexpr int STAGE = AB + NBR * KB;
+  constexpr int AI = BM / RPI / NW;             // A load instructions per wave per stage
+  constexpr int BI = NBR / RPI / NW;            // B load instructions per wave per stage
+  constexpr int NI = AI + BI;
+  static_assert(AI >= 1 && BI >= 1 && SM >= 1 && SN >= 1, "tile shape");
 
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
 
   if ((int)blockIdx.x >= a.num_work[0]) return;
   const int2 wk = a.work[blockIdx.x];
@@ -72,22 +103,22 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w / WAVES_N, wn = w % WAVES_N;
 
-  // Load assignment: instruction i of wave w fills LDS rows 8*(w*XI+i) ..+7;
-  // lane l writes physical chunk l%8 of row 8*(..)+l/8, which holds logical
-  // chunk (l%8) ^ (l/8).
-  const int lr = lane >> 3;
-  const uint32_t lcb = (uint32_t)(((lane & 7) ^ lr) * 16);
+  // Load assignment: instruction i of wave w fills LDS rows RPI*(w*XI+i) ..;
+  // lane l writes physical chunk l%CPR of row RPI*(..)+l/CPR, which holds
+  // logical chunk (l%CPR) ^ ((l/CPR)%CPR).
+  const int lr = lane / CPR;
+  const uint32_t lcb = (uint32_t)(((lane % CPR) ^ (lr % CPR)) * 16);
   uint32_t aoff[AI], boff[BI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    const int rA = (w * AI + i) * 8 + lr;
+    const int rA = (w * AI + i) * RPI + lr;
     const int r = r0 + (rA < rows ? rA : 0);
     const int64_t src = a.a_index ? (int64_t)a.a_index[r] : (int64_t)r;
     aoff[i] = (uint32_t)(src * a.lda * 2) + lcb;
   }
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
-    const int rB = (w * BI + i) * 8 + lr;
+    const int rB = (w * BI + i) * RPI + lr;
     int64_t wr;
     if constexpr (DUAL) {
       const int64_t nn = n0 + (rB & (OUTC - 1));
@@ -101,8 +132,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
   const char* Abase = static_cast<const char*>(a.A);
   const char* Bbase = static_cast<const char*>(a.B) + (int64_t)e * a.b_estride * 2;
 
-  auto issue = [&](int kt, char* dst) {
-    const uint32_t kb = (uint32_t)kt * 128u;
+  // Loads of stage kt into its buffer; past the end of K the last stage is
+  // reloaded (into a buffer nobody reads any more), so every step issues the
+  // same number of loads and the wait count is one constant.
+  const int nk = (int)(a.Kd / (KB / 2));
+  auto issue = [&](int kt) {
+    char* dst = lds + (kt % S) * STAGE;
+    const uint32_t kb = (uint32_t)min(kt, nk - 1) * (uint32_t)KB;
 #pragma unroll
     for (int i = 0; i < AI; ++i)
       lds_dma16(Abase + (aoff[i] + kb), dst + (w * AI + i) * 1024);
@@ -111,86 +147,98 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs a) {
       lds_dma16(Bbase + (boff[i] + kb), dst + AB + (w * BI + i) * 1024);
   };
 
-  f32x4 acc[NACC][SM][SN];
+  // v_mfma_f32_32x32x16_bf16 with the weights as operand 0: for a 32x32
+  // tile, lane l holds output row (token) l%32 and columns 8q + 4(l/32) + r,
+  // q, r = 0..3 (accumulator element 4q + r).  Each operand fragment is 16
+  // bytes per lane: row l%32, k = 8(l/32)..+8 of a 16-k slice.
+  f32x16 acc[NACC][SM][SN];
 #pragma unroll
   for (int q = 0; q < NACC; ++q)
 #pragma unroll
     for (int mi = 0; mi < SM; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < SN; ++ni) acc[q][mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ni = 0; ni < SN; ++ni) acc[q][mi][ni] = f32x16{};
 
-  const int g = lane >> 4, l16 = lane & 15;
-  // Fragment addresses (bytes inside a stage): row*128 + swizzled chunk.
-  const int arow = wm * WM + l16;
-  const int brow = wn * WN + l16;
-  int co[2];
+  const int l32 = lane & 31, h = lane >> 5;
+  // Fragment addresses (bytes inside a stage): row*KB + swizzled chunk; the
+  // 16-k slice t of the stage is chunk 2t + h.
+  const int arow = wm * WM + l32;
+  const int brow = wn * WN + l32;
+  int co[NT];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) co[s] = ((s * 4 + g) ^ (l16 & 7)) * 16;
+  for (int t = 0; t < NT; ++t) co[t] = ((2 * t + h) ^ (l32 % CPR)) * 16;
 
-  // One K step from one LDS stage: two sub-steps of 32 k.  A "group" is the
-  // NACC*SN MFMAs of one A fragment.  Reads are spread over the groups so that
-  // each one is issued a whole group before its use: the A fragments two
-  // groups ahead, the second sub-step's B fragments one per group of the first
-  // sub-step, and its first two A fragments during the last two groups.  Only
-  // the first sub-step's B fragments and first A fragments wait on LDS, once
-  // per stage.  Scheduling barriers keep that order.
+  // One K step from one LDS stage = NT 16-k slices.  A "group" is the NB
+  // MFMAs of one A fragment (NB*32 cycles of matrix core work).  Every LDS
+  // read is issued at least one group before its use: the next A fragment one
+  // group ahead, the next slice's B fragments spread over the current slice's
+  // groups.  Only the first slice's first reads wait on LDS, once per stage.
+  // Scheduling barriers keep this order.
   constexpr int NB = NACC * SN;
-  auto rdA = [&](const char* buf, int s, int mi) {
-    return *reinterpret_cast<const bf16x8*>(buf + (arow + mi * 16) * 128 + co[s]);
+  auto rdA = [&](const char* buf, int t, int mi) {
+    return *reinterpret_cast<const bf16x8*>(buf + (arow + mi * 32) * KB + co[t]);
   };
-  auto rdB = [&](const char* buf, int s, int j) {
-    return *reinterpret_cast<const bf16x8*>(buf + AB + ((j / SN) * OUTC + brow + (j % SN) * 16) * 128 + co[s]);
+  auto rdB = [&](const char* buf, int t, int j) {
+    return *reinterpret_cast<const bf16x8*>(buf + AB + ((j / SN) * OUTC + brow + (j % SN) * 32) * KB + co[t]);
   };
   auto compute = [&](const char* buf) {
-    bf16x8 fa0[SM], fa1[SM], fb0[NB], fb1[NB];
+    bf16x8 fb[2][NB], fa[2];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) fb0[j] = rdB(buf, 0, j);
-    fa0[0] = rdA(buf, 0, 0);
-    if (SM > 1) fa0[1] = rdA(buf, 0, 1);
+    for (int j = 0; j < NB; ++j) fb[0][j] = rdB(buf, 0, j);
+    fa[0] = rdA(buf, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int mi = 0; mi < SM; ++mi) {
-      if (mi + 2 < SM) fa0[mi + 2] = rdA(buf, 0, mi + 2);
-      if (mi + 2 == SM) fa1[0] = rdA(buf, 1, 0);
-      if (mi + 1 == SM && SM > 1) fa1[1] = rdA(buf, 1, 1);
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
-      for (int j = mi * NB / SM; j < (mi + 1) * NB / SM; ++j) fb1[j] = rdB(buf, 1, j);
+      for (int mi = 0; mi < SM; ++mi) {
+        const int g = t * SM + mi;  // group index in the stage
+        if (mi + 1 < SM)
+          fa[(g + 1) & 1] = rdA(buf, t, mi + 1);
+        else if (t + 1 < NT)
+          fa[(g + 1) & 1] = rdA(buf, t + 1, 0);
+        if (t + 1 < NT) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        acc[j / SN][mi][j % SN] =
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb0[j], fa0[mi], acc[j / SN][mi][j % SN], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+          for (int j = mi * NB / SM; j < (mi + 1) * NB / SM; ++j) fb[(t + 1) & 1][j] = rdB(buf, t + 1, j);
+        }
 #pragma unroll
-    for (int mi = 0; mi < SM; ++mi) {
-      if (mi + 2 < SM) fa1[mi + 2] = rdA(buf, 1, mi + 2);
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        acc[j / SN][mi][j % SN] =
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb1[j], fa1[mi], acc[j / SN][mi][j % SN], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < NB; ++j)
+          acc[j / SN][mi][j % SN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[t & 1][j], fa[g & 1],
+                                                                          acc[j / SN][mi][j % SN], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
-  const int nk = (int)(a.Kd / 64);
-  issue(0, lds);
+  // Step kt: wait for this wave's loads of stage kt (the S-2 later stages
+  // stay in flight), barrier (stage kt visible to all waves; all waves done
+  // with stage kt-1), issue stage kt+S-1 into the buffer of stage kt-1, then
+  // the MFMAs of stage kt.
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p) issue(p);
   for (int kt = 0; kt < nk; ++kt) {
-    wait_vm0();
-    __syncthreads();
-    if (kt + 1 < nk) issue(kt + 1, lds + ((kt + 1) & 1) * STAGE);
-    compute(lds + (kt & 1) * STAGE);
+    wait_vm<(S - 2) * NI>();
+    barrier_lds();
+    issue(kt + S - 1);
+    compute(lds + (kt % S) * STAGE);
   }
-  wait_vm0();  // no LDS DMA may outlive the workgroup
+  wait_vm<0>();  // no LDS DMA may outlive the workgroup
 
   const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;
 #pragma unroll
   for (int mi = 0; mi < SM; ++mi) {
-    const int m = wm * WM + mi * 16 + l16;
+    const int m = wm * WM + mi * 32 + l32;
     if (m >= rows) continue;
     const RowCtx rc = row_ctx<EPI>(a, r0 + m);
 #pragma unroll
     for (int ni = 0; ni < SN; ++ni)
-      epilogue4<uint16_t, EPI>(a, rc, n0 + wn * WN + ni * 16 + 4 * g, acc[0][mi][ni], acc[NACC - 1][mi][ni], bias);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x16& c0 = acc[0][mi][ni];
+        const f32x16& c1 = acc[NACC - 1][mi][ni];
+        const f32x4 v0{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
+        const f32x4 v1{c1[4 * q4], c1[4 * q4 + 1], c1[4 * q4 + 2], c1[4 * q4 + 3]};
+        epilogue4<uint16_t, EPI>(a, rc, n0 + wn * WN + ni * 32 + 8 * q4 + 4 * h, v0, v1, bias);
+      }
   }
 }
 
@@ -198,13 +246,13 @@ template <int EPI>
 hipError_t launch_rows(int var, const GemmArgs& a, hipStream_t s) {
   switch (var) {
     case VAR_BF16_M256:
-      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 256>), dim3(a.max_work), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, ShapeM256>), dim3(a.max_work), dim3(ShapeM256::NW * 64), 0, s, a);
       break;
     case VAR_BF16_M128:
-      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 128>), dim3(a.max_work), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, ShapeM128>), dim3(a.max_work), dim3(ShapeM128::NW * 64), 0, s, a);
       break;
     default:
-      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 32>), dim3(a.max_work), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, ShapeM32>), dim3(a.max_work), dim3(ShapeM32::NW * 64), 0, s, a);
       break;
   }
   return hipGetLastError();

@@ -40,7 +40,7 @@ def device_inputs(inp: dict, device="cuda") -> dict:
                                                        "up_bias", "down_bias")}
 
 
-def gpu_forward(inp: dict, dev_inp: dict | None = None, *, deterministic=False, out_dtype=None) -> dict:
+def gpu_forward(inp: dict, dev_inp: dict | None = None, *, deterministic=True, out_dtype=None) -> dict:
     import torch
     import sparse_mixture_experts_02_amd as moe
     c = inp["cfg"]
