@@ -12,9 +12,11 @@
 //
 // Data path: global_load_lds_dwordx4 writes each 16-byte chunk straight from
 // HBM/L2 into LDS (no staging registers).  LDS holds S stages of KB bytes of
-// K per row; rows are KB bytes with the 16-byte chunk index XOR-ed with the
-// low row bits, so a wave's fragment read of 32 rows at one chunk spreads over
-// the banks.  A lane of a load instruction writes LDS byte 16*lane of a
+// K per row; rows are KB bytes with the 16-byte chunk index XOR-ed with
+// bits 1.. of the row index.  gfx950 LDS serves 256 bytes per clock; a
+// 32x32 fragment read (32 rows, two chunks) is conflict-free under this
+// swizzle, while XOR-ing with the low row bits halves its throughput
+// (measured with a probe of the two patterns).  A lane of a load instruction writes LDS byte 16*lane of a
 // block of 1024/KB rows, so it loads the global chunk the swizzle puts there.
 // The loads of a stage are issued S-1 steps before it is consumed; one
 // barrier per step, waited on only for the loads of the stage being
@@ -62,7 +64,7 @@ struct Shape {
 // tiles two 64 KB stages with 8 waves beat deeper pipelines of 32 KB stages
 // (which need twice the barriers); the decode tile is a weight stream and
 // wants more bytes in flight.
-using ShapeM256 = Shape<256, 8, 2, 128, 2>;  // 2 x 64 KB of LDS
+using ShapeM256 = Shape<256, 8, 4, 128, 2>;  // 2 x 64 KB of LDS
 using ShapeM128 = Shape<128, 4, 2, 128, 2>;  // 2 x 48 KB
 using ShapeM32 = Shape<32, 4, 1, 128, 4>;    // 4 x 36 KB
 
@@ -104,17 +106,18 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   const int wm = w / WAVES_N, wn = w % WAVES_N;
 
   // Load assignment: instruction i of wave w fills LDS rows RPI*(w*XI+i) ..;
-  // lane l writes physical chunk l%CPR of row RPI*(..)+l/CPR, which holds
-  // logical chunk (l%CPR) ^ ((l/CPR)%CPR).
+  // lane l writes physical chunk l%CPR of row r = RPI*(..)+l/CPR, which holds
+  // logical chunk (l%CPR) ^ swz(r).
   const int lr = lane / CPR;
-  const uint32_t lcb = (uint32_t)(((lane % CPR) ^ (lr % CPR)) * 16);
+  // physical chunk of logical chunk c in row r: c ^ swz(r)
+  auto swz = [](int r) { return (r >> 1) & (CPR - 1); };
   uint32_t aoff[AI], boff[BI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
     const int rA = (w * AI + i) * RPI + lr;
     const int r = r0 + (rA < rows ? rA : 0);
     const int64_t src = a.a_index ? (int64_t)a.a_index[r] : (int64_t)r;
-    aoff[i] = (uint32_t)(src * a.lda * 2) + lcb;
+    aoff[i] = (uint32_t)(src * a.lda * 2) + (uint32_t)(((lane % CPR) ^ swz(rA)) * 16);
   }
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
       const int64_t nn = n0 + rB;
       wr = nn < N ? nn : N - 1;
     }
-    boff[i] = (uint32_t)(wr * a.ldb * 2) + lcb;
+    boff[i] = (uint32_t)(wr * a.ldb * 2) + (uint32_t)(((lane % CPR) ^ swz(rB)) * 16);
   }
   const char* Abase = static_cast<const char*>(a.A);
   const char* Bbase = static_cast<const char*>(a.B) + (int64_t)e * a.b_estride * 2;
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   const int brow = wn * WN + l32;
   int co[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) co[t] = ((2 * t + h) ^ (l32 % CPR)) * 16;
+  for (int t = 0; t < NT; ++t) co[t] = ((2 * t + h) ^ swz(l32)) * 16;  // row bases are multiples of 32
 
   // One K step from one LDS stage = NT 16-k slices.  A "group" is the NB
   // MFMAs of one A fragment (NB*32 cycles of matrix core work).  Every LDS
@@ -213,13 +216,17 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   // stay in flight), barrier (stage kt visible to all waves; all waves done
   // with stage kt-1), issue stage kt+S-1 into the buffer of stage kt-1, then
   // the MFMAs of stage kt.
+  // A wave whose rows all lie past the end of the expert's segment (the last
+  // row tile of an expert is usually partial) skips its MFMAs; it still loads
+  // and meets every barrier.
+  const bool busy = wm * WM < rows;
 #pragma unroll
   for (int p = 0; p < S - 1; ++p) issue(p);
   for (int kt = 0; kt < nk; ++kt) {
     wait_vm<(S - 2) * NI>();
     barrier_lds();
     issue(kt + S - 1);
-    compute(lds + (kt % S) * STAGE);
+    if (busy) compute(lds + (kt % S) * STAGE);
   }
   wait_vm<0>();  // no LDS DMA may outlive the workgroup
 
