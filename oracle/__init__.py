@@ -51,6 +51,15 @@ def _load():
         lib.oracle_combine.restype = ctypes.c_int
         lib.oracle_param_count.argtypes = [I64, I64, I32, I32, I32, I32]
         lib.oracle_param_count.restype = ctypes.c_int64
+        lib.oracle_route.argtypes = [I64, I64, I32, I32, I32, I32, P, P, P, P, I64, P, P, ctypes.c_double, P, P, P,
+                                     P, P, I32]
+        lib.oracle_route.restype = ctypes.c_int
+        lib.oracle_capacity_slots.argtypes = [I64, I32, I32, ctypes.c_double]
+        lib.oracle_capacity_slots.restype = ctypes.c_int64
+        lib.oracle_capacity.argtypes = [I64, I32, I32, I64, I64, P, P]
+        lib.oracle_capacity.restype = ctypes.c_int
+        lib.oracle_experts.argtypes = [I64, I64, I64, I32, I32, I32, I32, P, P, P, P, P, P, I64, P, P, P, P, I32]
+        lib.oracle_experts.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -145,3 +154,148 @@ def combine(probs, expert_outs, *, top_k, norm=True) -> dict:
 def param_count(D, F, E, *, act="swiglu", expert_biases=False, router_bias=False) -> int:
     return int(_load().oracle_param_count(D, F, E, SWIGLU if act == "swiglu" else RELU,
                                           int(bool(expert_biases)), int(bool(router_bias))))
+
+
+# ------------------------------------------------------------ routing options
+def route(x, router, *, top_k, norm=True, router_bias=None, tokens=None, replay=None, replay_mask=None,
+          threshold=0.0, nthreads=None) -> dict:
+    """Router part for the given tokens (default all): logits, probs, sel,
+    weights and kept flags, with routing replay (``replay`` (n,K), optional
+    ``replay_mask`` (n) bool) and the dynamic threshold.  See oracle_route in
+    moe_oracle.c for the passages each option follows."""
+    lib = _load()
+    x2 = np.ascontiguousarray(x).reshape(-1, np.shape(x)[-1])
+    T, D = x2.shape
+    router = np.ascontiguousarray(router)
+    E = router.shape[0]
+    dt = _dtype_code(x2)
+    if _dtype_code(router) != dt or router.shape != (E, D):
+        raise ValueError("router must be (E,D) in the dtype of x")
+    rb = None if router_bias is None else np.ascontiguousarray(router_bias, dtype=np.float32)
+    if tokens is not None:
+        tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+        n = tokens.shape[0]
+    else:
+        n = T
+    if replay is not None:
+        replay = np.ascontiguousarray(replay, dtype=np.int64).reshape(n, top_k)
+    if replay_mask is not None:
+        replay_mask = np.ascontiguousarray(replay_mask, dtype=np.uint8).reshape(n)
+    sel = np.empty((n, top_k), np.int64)
+    w = np.empty((n, top_k), np.float64)
+    logits = np.empty((n, E), np.float64)
+    probs = np.empty((n, E), np.float64)
+    kept = np.empty((n, top_k), np.uint8)
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    rc = lib.oracle_route(T, D, E, top_k, int(bool(norm)), dt, _ptr(x2), _ptr(router), _ptr(rb), _ptr(tokens), n,
+                          _ptr(replay), _ptr(replay_mask), float(threshold), _ptr(sel), _ptr(w), _ptr(logits),
+                          _ptr(probs), _ptr(kept), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_route failed with code %d" % rc)
+    return dict(sel=sel, weights=w, logits=logits, probs=probs, kept=kept.astype(bool))
+
+
+def capacity_slots(seq_len, top_k, num_experts, capacity_factor) -> int:
+    """Slots per expert per sequence for a capacity factor (oracle_capacity_slots)."""
+    return int(_load().oracle_capacity_slots(int(seq_len), int(top_k), int(num_experts), float(capacity_factor)))
+
+
+def capacity(sel, kept, *, num_experts, seq_len, slots) -> np.ndarray:
+    """Capacity drops over whole sequences; returns the updated kept flags (T,K)."""
+    sel = np.ascontiguousarray(sel, dtype=np.int64)
+    T, K = sel.shape
+    k8 = np.ascontiguousarray(kept, dtype=np.uint8).copy()
+    rc = _load().oracle_capacity(T, K, int(num_experts), int(seq_len), int(slots), _ptr(sel), _ptr(k8))
+    if rc != 0:
+        raise ValueError("oracle_capacity failed with code %d" % rc)
+    return k8.astype(bool)
+
+
+def experts(x, gate_up, down, sel, weights, kept=None, *, act="swiglu", up_bias=None, down_bias=None, tokens=None,
+            nthreads=None) -> np.ndarray:
+    """Expert part for the given tokens with given sel/weights/kept (rows per evaluated token)."""
+    lib = _load()
+    x2 = np.ascontiguousarray(x).reshape(-1, np.shape(x)[-1])
+    T, D = x2.shape
+    gate_up, down = np.ascontiguousarray(gate_up), np.ascontiguousarray(down)
+    E, _, F = down.shape
+    dt = _dtype_code(x2)
+    sel = np.ascontiguousarray(sel, dtype=np.int64)
+    n, K = sel.shape
+    weights = np.ascontiguousarray(weights, dtype=np.float64)
+    k8 = None if kept is None else np.ascontiguousarray(kept, dtype=np.uint8)
+    ub, db = (None if b is None else np.ascontiguousarray(b, dtype=np.float32) for b in (up_bias, down_bias))
+    if tokens is not None:
+        tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+        if tokens.shape[0] != n:
+            raise ValueError("one sel row per evaluated token")
+    elif n > T:
+        raise ValueError("more rows than tokens")
+    out = np.empty((n, D), np.float64)
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    rc = lib.oracle_experts(T, D, F, E, K, SWIGLU if act == "swiglu" else RELU, dt, _ptr(x2), _ptr(gate_up),
+                            _ptr(down), _ptr(ub), _ptr(db), _ptr(tokens), n, _ptr(sel), _ptr(weights), _ptr(k8),
+                            _ptr(out), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_experts failed with code %d" % rc)
+    return out
+
+
+def balance_stats(probs, sel, weights) -> dict:
+    """Router statistics and the four balancing objectives of the ES-MoE "API"
+    page, section "Balancing objectives", over the T tokens of one call.
+
+    probs (T,E) is the full softmax; the gate (T,E) holds each token's routing
+    weights at its selected experts (the top-k selection renormalised) and 0
+    elsewhere.  The usage u is the per-expert mean, normalised to sum to one:
+      switch       = E * sum_i mean(probs)_i * mean(gate > 0)_i
+      gshard       = E * sum_i u_i^2                   (u from the gate)
+      master       = (1/E) * sum_i (u_i - 1/E)^2        (u from the gate)
+      gshard_probs = E * sum_i u_i^2                   (u from probs)
+    All in float64.
+    """
+    probs = np.asarray(probs, dtype=np.float64)
+    sel = np.asarray(sel, dtype=np.int64)
+    weights = np.asarray(weights, dtype=np.float64)
+    T, E = probs.shape
+    gate = np.zeros((T, E), np.float64)
+    for k in range(sel.shape[1]):
+        np.add.at(gate, (np.arange(T), sel[:, k]), weights[:, k])
+    mean_probs = probs.mean(axis=0)
+    mean_gate = gate.mean(axis=0)
+    frac_routed = (gate > 0).mean(axis=0)
+    u_gate = mean_gate / mean_gate.sum()
+    u_probs = mean_probs / mean_probs.sum()
+    return dict(mean_probs=mean_probs, mean_gate=mean_gate, frac_routed=frac_routed,
+                switch=float(E * np.sum(mean_probs * frac_routed)),
+                gshard=float(E * np.sum(u_gate ** 2)),
+                master=float(np.sum((u_gate - 1.0 / E) ** 2) / E),
+                gshard_probs=float(E * np.sum(u_probs ** 2)))
+
+
+def forward_routed(inp: dict, *, tokens=None, replay=None, replay_mask=None, threshold=0.0, capacity_factor=None,
+                   seq_len=None, nthreads=None) -> dict:
+    """The layer with routing options on a ``workloads.generate`` dict.
+
+    Routing (replay, dynamic threshold) and capacity drops are decided over
+    all T tokens; the experts are evaluated for ``tokens`` (default all).
+    Returns out (n,D) for the evaluated tokens; sel, weights, kept, logits,
+    probs for all T tokens; the capacity slot count (or None); stats.
+    """
+    c = inp["cfg"]
+    r = route(inp["x"], inp["router"], top_k=c["K"], norm=c["norm"], router_bias=inp.get("router_bias"),
+              replay=replay, replay_mask=replay_mask, threshold=threshold, nthreads=nthreads)
+    T = r["sel"].shape[0]
+    slots = None
+    if capacity_factor is not None:
+        L = T if seq_len is None else int(seq_len)
+        slots = capacity_slots(L, c["K"], c["E"], capacity_factor)
+        r["kept"] = capacity(r["sel"], r["kept"], num_experts=c["E"], seq_len=L, slots=slots)
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    out = experts(inp["x"], inp["gate_up"], inp["down"], r["sel"][tok], r["weights"][tok], r["kept"][tok],
+                  act=c["act"], up_bias=inp.get("up_bias"), down_bias=inp.get("down_bias"), tokens=tok,
+                  nthreads=nthreads)
+    r.update(out=out, slots=slots, stats=balance_stats(r["probs"], r["sel"], r["weights"]))
+    return r
