@@ -146,12 +146,89 @@ moe_status moe_dispatch(const moe_desc* d, const void* x, const void* router, co
                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_token,
                         int32_t* sorted_slot, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Routing options (all off when the pointer to this struct is NULL, or when
+ * every field is 0 / NULL).
+ *
+ *   replay_experts   (T,K) int64 device, or NULL.  Routing replay (the Dew
+ *                    "Mixture of experts" concepts page, section "Router
+ *                    behavior"): a covered token uses the recorded experts in
+ *                    place of its own top-k, in the recorded order, and its
+ *                    weights still come from this forward's probabilities
+ *                    (p_rec / (sum p_rec + 1e-9) when norm_topk).  A token
+ *                    whose record holds an index outside [0,E) is not
+ *                    covered.  A record may name one expert twice.
+ *   replay_mask      (T) uint8 device, or NULL: nonzero where the record covers
+ *                    the token (NULL: it covers every token).  An uncovered
+ *                    token keeps the router's own top-k.
+ *   dynamic_threshold >= 0; 0 is off.  The ES-MoE "API" page, settings table
+ *                    of "ESMoE": a slot k >= 1 whose renormalised weight is
+ *                    below the threshold is dropped (compared in fp32), the
+ *                    leader (k = 0) is always kept, and the kept weights are
+ *                    renormalised to sum to one.  Needs norm_topk = 1.  A
+ *                    dropped slot keeps its expert in selected_experts, gets
+ *                    weight 0 and adds nothing.
+ *   capacity_factor  >= 0; 0 is off (every slot kept).  The Dew page, section
+ *                    "Expert computation and placement": each sequence of
+ *                    seq_len tokens keeps floor(max(ceil(seq_len*K/E) * cf,
+ *                    cf)) slots per expert, the first in token order (t, then
+ *                    k); a slot dropped by the threshold takes none.  A slot
+ *                    dropped for capacity keeps its weight in routing_weights
+ *                    but adds nothing to out.
+ *   seq_len          tokens per sequence for the capacity; 0 means T.  T must
+ *                    be a multiple of it.
+ *   kept             (T,K) uint8 device out, or NULL: 1 where the slot
+ *                    contributes to out, 0 where the threshold or the
+ *                    capacity dropped it.
+ *   stats            (MOE_STATS_LEN(E)) fp32 device out, or NULL.  Router
+ *                    statistics and the balancing objectives of the ES-MoE
+ *                    "API" page, section "Balancing objectives", over the T
+ *                    tokens of the call.  With gate (T,E) = each token's
+ *                    routing weights at its selected experts (after the
+ *                    threshold, before the capacity) and u = the per-expert
+ *                    mean normalised to sum to one:
+ *                      [0,E)    mean over tokens of p
+ *                      [E,2E)   mean over tokens of the gate
+ *                      [2E,3E)  mean over tokens of [gate > 0]
+ *                      [3E]     switch       = E * sum_i mean(p)_i * mean(gate>0)_i
+ *                      [3E+1]   gshard       = E * sum_i u_i^2 (u of the gate)
+ *                      [3E+2]   master       = (1/E) * sum_i (u_i - 1/E)^2
+ *                      [3E+3]   gshard_probs = E * sum_i u_i^2 (u of p)
+ *                    Summed in a fixed order: bitwise reproducible.
+ * expert_counts then counts the slots each expert computes (after drops).
+ * Invalid values (negative or NaN threshold / factor, a threshold without
+ * norm_topk, seq_len < 0 or not dividing T) return MOE_EINVAL.
+ */
+typedef struct {
+  const int64_t* replay_experts;
+  const uint8_t* replay_mask;
+  float dynamic_threshold;
+  double capacity_factor;
+  int64_t seq_len;
+  uint8_t* kept;
+  float* stats;
+} moe_routing;
+#define MOE_STATS_LEN(E) (3 * (E) + 4)
+/* moe_forward with routing options r (NULL: exactly moe_forward). */
+moe_status moe_forward_routed(const moe_desc* d, const moe_routing* r, const void* x, const void* router,
+                              const void* gate_up_proj, const void* down_proj, const float* router_bias,
+                              const float* up_bias, const float* down_bias, void* out, int64_t* selected_experts,
+                              float* routing_weights, float* router_logits, int32_t* expert_counts,
+                              void* workspace, size_t workspace_bytes, void* stream);
+/* moe_dispatch with routing options r (NULL: exactly moe_dispatch).  The
+ * sorted order then holds only the kept slots; expert_offsets[E] is their
+ * number. */
+moe_status moe_dispatch_routed(const moe_desc* d, const moe_routing* r, const void* x, const void* router,
+                               const float* router_bias, int64_t* selected_experts, float* routing_weights,
+                               float* router_logits, int32_t* expert_counts, int32_t* expert_offsets,
+                               int32_t* sorted_token, int32_t* sorted_slot, void* workspace, size_t workspace_bytes,
+                               void* stream);
 /* Human-readable text of a status code (static storage). */
 const char* moe_status_string(moe_status s);
 
 /* ABI version of this header (bumped on any signature change). */
 int32_t moe_abi_version(void);
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

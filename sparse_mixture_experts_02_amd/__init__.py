@@ -42,6 +42,18 @@ class MoeDesc(ctypes.Structure):
                 ("deterministic", ctypes.c_int32)]
 
 
+class MoeRouting(ctypes.Structure):
+    """Mirror of ``moe_routing`` in include/moe.h."""
+    _fields_ = [("replay_experts", ctypes.c_void_p), ("replay_mask", ctypes.c_void_p),
+                ("dynamic_threshold", ctypes.c_float), ("capacity_factor", ctypes.c_double),
+                ("seq_len", ctypes.c_int64), ("kept", ctypes.c_void_p), ("stats", ctypes.c_void_p)]
+
+
+def stats_len(E: int) -> int:
+    """Length of the statistics vector (MOE_STATS_LEN)."""
+    return 3 * int(E) + 4
+
+
 class MoEError(RuntimeError):
     """A HIP launch or runtime failure reported by the library."""
 
@@ -73,6 +85,11 @@ def load_library():
         lib.moe_forward_timed.restype = ctypes.c_int
         lib.moe_dispatch.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
         lib.moe_dispatch.restype = ctypes.c_int
+        R = ctypes.POINTER(MoeRouting)
+        lib.moe_forward_routed.argtypes = [D, R, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+        lib.moe_forward_routed.restype = ctypes.c_int
+        lib.moe_dispatch_routed.argtypes = [D, R, P, P, P, P, P, P, P, P, P, P, P, S, P]
+        lib.moe_dispatch_routed.restype = ctypes.c_int
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
         lib.moe_abi_version.argtypes = []
@@ -121,6 +138,26 @@ def moe_dispatch(desc, x, router, router_bias, selected_experts, routing_weights
     return load_library().moe_dispatch(ctypes.byref(desc), x, router, router_bias, selected_experts,
                                        routing_weights, router_logits, expert_counts, expert_offsets, sorted_token,
                                        sorted_slot, workspace, workspace_bytes, stream)
+
+
+def moe_forward_routed(desc, routing, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out,
+                       selected_experts, routing_weights, router_logits, expert_counts, workspace, workspace_bytes,
+                       stream) -> int:
+    """Raw call; ``routing`` is a MoeRouting or None."""
+    r = ctypes.byref(routing) if routing is not None else None
+    return load_library().moe_forward_routed(ctypes.byref(desc), r, x, router, gate_up_proj, down_proj, router_bias,
+                                             up_bias, down_bias, out, selected_experts, routing_weights,
+                                             router_logits, expert_counts, workspace, workspace_bytes, stream)
+
+
+def moe_dispatch_routed(desc, routing, x, router, router_bias, selected_experts, routing_weights, router_logits,
+                        expert_counts, expert_offsets, sorted_token, sorted_slot, workspace, workspace_bytes,
+                        stream) -> int:
+    """Raw call; ``routing`` is a MoeRouting or None."""
+    r = ctypes.byref(routing) if routing is not None else None
+    return load_library().moe_dispatch_routed(ctypes.byref(desc), r, x, router, router_bias, selected_experts,
+                                              routing_weights, router_logits, expert_counts, expert_offsets,
+                                              sorted_token, sorted_slot, workspace, workspace_bytes, stream)
 
 
 def _check(status: int) -> None:
@@ -184,16 +221,41 @@ def _prepare(x, router, gate_up_proj, down_proj, top_k, act):
     return D, F, E
 
 
+def _routing(T, top_k, dev, replay, replay_mask, dynamic_threshold, capacity_factor, seq_len, kept, stats):
+    """A MoeRouting for the options (None when every option is off), plus the
+    device tensors it points to (kept alive by the caller)."""
+    torch = _torch()
+    if replay is None and not dynamic_threshold and capacity_factor is None and kept is None and stats is None:
+        return None, []
+    keep = []
+    rep = msk = None
+    if replay is not None:
+        rep = replay.to(device=dev, dtype=torch.int64).reshape(T, top_k).contiguous()
+        keep.append(rep)
+        if replay_mask is not None:
+            msk = replay_mask.to(device=dev).reshape(T).ne(0).to(torch.uint8).contiguous()
+            keep.append(msk)
+    r = MoeRouting(replay_experts=_ptr(rep), replay_mask=_ptr(msk), dynamic_threshold=float(dynamic_threshold or 0.0),
+                   capacity_factor=float(capacity_factor or 0.0), seq_len=int(seq_len or 0), kept=_ptr(kept),
+                   stats=_ptr(stats))
+    return r, keep
+
+
 def forward(x, router, gate_up_proj, down_proj, *, top_k, norm_topk_prob=True, act="silu", router_bias=None,
             up_bias=None, down_bias=None, out_dtype=None, deterministic=True, return_logits=False,
-            return_counts=False, workspace=None):
+            return_counts=False, workspace=None, replay=None, replay_mask=None, dynamic_threshold=0.0,
+            capacity_factor=None, seq_len=None, return_kept=False, return_stats=False):
     """Layer forward on the device of x.
 
     Returns (out with the shape of x, selected_experts int64 (T,K),
-    routing_weights fp32 (T,K)) plus router_logits (T,E) and expert_counts (E)
-    when requested.  ``out_dtype`` defaults to float32.  ``deterministic``
-    (default) sums each token's K expert rows in k order; False adds them with
-    fp32 atomics instead.
+    routing_weights fp32 (T,K)) plus, in this order and when requested,
+    router_logits (T,E), expert_counts (E), kept (T,K) bool and the
+    statistics vector (3E+4) fp32.  ``out_dtype`` defaults to float32.
+    ``deterministic`` (default) sums each token's K expert rows in k order;
+    False adds them with fp32 atomics instead.  Routing options (see
+    ``moe_routing`` in include/moe.h): ``replay`` (T,K) recorded experts with
+    an optional ``replay_mask`` (T); ``dynamic_threshold``; ``capacity_factor``
+    over sequences of ``seq_len`` tokens (default: all T).
     """
     torch = _torch()
     D, F, E = _prepare(x, router, gate_up_proj, down_proj, top_k, act)
@@ -215,22 +277,35 @@ def forward(x, router, gate_up_proj, down_proj, *, top_k, norm_topk_prob=True, a
     biases = [None if b is None else b.to(device=dev, dtype=torch.float32).contiguous()
               for b in (router_bias, up_bias, down_bias)]
     stream = torch.cuda.current_stream(dev).cuda_stream
-    _check(moe_forward(desc, _ptr(x2), _ptr(router.contiguous()), _ptr(gate_up_proj.contiguous()),
-                       _ptr(down_proj.contiguous()), *(_ptr(b) for b in biases), _ptr(out), _ptr(sel), _ptr(w),
-                       _ptr(logits), _ptr(counts), _ptr(workspace), nbytes, stream))
+    kept = torch.empty((T, top_k), dtype=torch.uint8, device=dev) if return_kept else None
+    stats = torch.empty((stats_len(E),), dtype=torch.float32, device=dev) if return_stats else None
+    rt, _alive = _routing(T, top_k, dev, replay, replay_mask, dynamic_threshold, capacity_factor, seq_len, kept, stats)
+    args = (_ptr(x2), _ptr(router.contiguous()), _ptr(gate_up_proj.contiguous()), _ptr(down_proj.contiguous()),
+            *(_ptr(b) for b in biases), _ptr(out), _ptr(sel), _ptr(w), _ptr(logits), _ptr(counts), _ptr(workspace),
+            nbytes, stream)
+    if rt is None:
+        _check(moe_forward(desc, *args))
+    else:
+        _check(moe_forward_routed(desc, rt, *args))
     res = [out.reshape(*lead, D), sel, w]
     if return_logits:
         res.append(logits)
     if return_counts:
         res.append(counts)
+    if return_kept:
+        res.append(kept.bool())
+    if return_stats:
+        res.append(stats)
     return tuple(res)
 
 
-def dispatch(x, router, *, top_k, norm_topk_prob=True, router_bias=None, num_experts=None, F=1):
-    """Router plus the stable sort into expert order.
+def dispatch(x, router, *, top_k, norm_topk_prob=True, router_bias=None, num_experts=None, F=1, replay=None,
+             replay_mask=None, dynamic_threshold=0.0, capacity_factor=None, seq_len=None):
+    """Router plus the stable sort into expert order (of the kept slots when
+    a routing option drops some).
 
     Returns dict(selected_experts, routing_weights, router_logits,
-    expert_counts, expert_offsets, sorted_token, sorted_slot).
+    expert_counts, expert_offsets, sorted_token, sorted_slot, kept).
     """
     torch = _torch()
     D = x.shape[-1]
@@ -251,14 +326,18 @@ def dispatch(x, router, *, top_k, norm_topk_prob=True, router_bias=None, num_exp
     ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
     rb = None if router_bias is None else router_bias.to(device=dev, dtype=torch.float32).contiguous()
     stream = torch.cuda.current_stream(dev).cuda_stream
-    _check(moe_dispatch(desc, _ptr(x2), _ptr(router.contiguous()), _ptr(rb), _ptr(r["selected_experts"]),
-                        _ptr(r["routing_weights"]), _ptr(r["router_logits"]), _ptr(r["expert_counts"]),
-                        _ptr(r["expert_offsets"]), _ptr(r["sorted_token"]), _ptr(r["sorted_slot"]), _ptr(ws),
-                        nbytes, stream))
+    kept = torch.empty((T, top_k), dtype=torch.uint8, device=dev)
+    rt, _alive = _routing(T, top_k, dev, replay, replay_mask, dynamic_threshold, capacity_factor, seq_len, kept, None)
+    _check(moe_dispatch_routed(desc, rt, _ptr(x2), _ptr(router.contiguous()), _ptr(rb), _ptr(r["selected_experts"]),
+                               _ptr(r["routing_weights"]), _ptr(r["router_logits"]), _ptr(r["expert_counts"]),
+                               _ptr(r["expert_offsets"]), _ptr(r["sorted_token"]), _ptr(r["sorted_slot"]),
+                               _ptr(ws), nbytes, stream))
+    r["kept"] = kept.bool()
     return r
 
 
 MOE_STAGE_EVENTS = 6
 
-__all__ = ["MoeDesc", "MoEError", "load_library", "moe_forward", "moe_forward_timed", "moe_dispatch", "moe_workspace_bytes",
-           "moe_status_string", "moe_abi_version", "make_desc", "forward", "dispatch", "LIB_PATH"]
+__all__ = ["MoeDesc", "MoeRouting", "MoEError", "load_library", "moe_forward", "moe_forward_timed",
+           "moe_forward_routed", "moe_dispatch", "moe_dispatch_routed", "moe_workspace_bytes", "moe_status_string",
+           "moe_abi_version", "make_desc", "stats_len", "forward", "dispatch", "LIB_PATH"]

@@ -8,6 +8,9 @@
 //           offsets, each chunk's starting row inside every segment, and the
 //           work lists of the grouped GEMMs (empty experts get no item, so
 //           they launch no MFMA work)
+// Assignments whose expert is the sentinel E (dropped by the dynamic
+// threshold or the capacity) take no row.
+//
 //   scatter one block per chunk: the chunk is walked in order; inside a wave
 //           equal experts are found with nine ballots (expert id bits plus a
 //           validity bit) and ranked by popcount, and waves are ordered
@@ -32,7 +35,10 @@ __global__ __launch_bounds__(kThreads) void count_kernel(DispatchArgs a) {
   __syncthreads();
   const int64_t beg = (int64_t)blockIdx.x * kDispatchChunk;
   const int64_t end = min(a.M, beg + kDispatchChunk);
-  for (int64_t i = beg + tid; i < end; i += kThreads) atomicAdd(&hist[a.sel32[i]], 1);
+  for (int64_t i = beg + tid; i < end; i += kThreads) {
+    const int e = a.sel32[i];
+    if (e < a.E) atomicAdd(&hist[e], 1);  // e == E: a dropped assignment
+  }
   __syncthreads();
   for (int e = tid; e < a.E; e += kThreads) a.chunk_counts[(int64_t)blockIdx.x * a.E + e] = hist[e];
 }
@@ -170,8 +176,9 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(DispatchArgs a) {
   const uint64_t below = (1ull << lane) - 1ull;
   for (int64_t base = beg; base < end; base += kThreads) {
     const int64_t i = base + tid;
-    const bool valid = i < end;
-    const int e = valid ? a.sel32[i] : kMaxExperts;   // the sentinel only matches itself
+    const int ei = i < end ? a.sel32[i] : E;
+    const bool valid = ei < E;                        // E: past the end, or a dropped assignment
+    const int e = valid ? ei : kMaxExperts;           // the sentinel only matches itself
     uint64_t same = ~0ull;
 #pragma unroll
     for (int bit = 0; bit < 9; ++bit) {
@@ -203,7 +210,47 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(DispatchArgs a) {
   }
 }
 
+// Capacity (the Dew "Mixture of experts" page, section "Expert computation
+// and placement", capacity_factor): each sequence keeps at most `slots`
+// assignments per expert, the first in token order.  In the stable sorted
+// order an expert's rows from one sequence are contiguous and in (t, k)
+// order, so a row's rank among them is its distance to the first row of the
+// segment whose token is in the same sequence (a binary search).
+__global__ __launch_bounds__(kThreads) void capacity_kernel(CapacityArgs a) {
+  __shared__ int offs[kMaxExperts + 1];
+  const int E = a.E;
+  for (int e = threadIdx.x; e <= E; e += kThreads) offs[e] = a.offsets[e];
+  __syncthreads();
+  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (r >= offs[E]) return;
+  // expert: the last e with offs[e] <= r
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offs[mid] <= r) lo = mid; else hi = mid;
+  }
+  const int64_t t = a.sorted_tok[r];
+  const int64_t s0 = t - t % a.seq_len;
+  int64_t b = offs[lo], c = r;  // first row in [b, r] whose token is >= s0
+  while (b < c) {
+    const int64_t mid = (b + c) >> 1;
+    if (a.sorted_tok[mid] < s0) b = mid + 1; else c = mid;
+  }
+  if (r - b >= a.slots) {
+    const int32_t slot = a.sorted_slot[r];
+    a.sel32[slot] = E;
+    if (a.kept) a.kept[slot] = 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_capacity(const CapacityArgs& a, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((a.M + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(capacity_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;

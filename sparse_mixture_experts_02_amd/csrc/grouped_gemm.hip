@@ -231,6 +231,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
       const int64_t t = (i * 4) / D, d = i * 4 - t * D;
       float4 s = {0.f, 0.f, 0.f, 0.f};
       for (int k = 0; k < a.K; ++k) {
+        if (a.slot_expert && a.slot_expert[t * a.K + k] >= a.E) continue;
         const float4 v = *reinterpret_cast<const float4*>(a.src + (t * a.K + k) * D + d);
         s.x += v.x;
         s.y += v.y;
@@ -252,7 +253,8 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
   for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * kThreads) {
     const int64_t t = idx / D, d = idx - t * D;
     float s = 0.f;
-    for (int k = 0; k < a.K; ++k) s += a.src[(t * a.K + k) * D + d];
+    for (int k = 0; k < a.K; ++k)
+      if (!a.slot_expert || a.slot_expert[t * a.K + k] < a.E) s += a.src[(t * a.K + k) * D + d];
     if (a.out_bf16)
       static_cast<uint16_t*>(a.out)[idx] = (uint16_t)f32_to_bf16_bits(s);
     else

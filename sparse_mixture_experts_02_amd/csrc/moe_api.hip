@@ -6,6 +6,7 @@
 #include "moe.h"
 
 #include <limits.h>
+#include <math.h>
 
 #include "moe_common.h"
 
@@ -28,8 +29,8 @@ struct Layout {
   int32_t nchunks = 0;
   GemmPlan g1, g2;
   size_t sel32 = 0, chunk_counts = 0, chunk_base = 0, counts = 0, offsets = 0, work1 = 0, work2 = 0,
-         num_work = 0, sorted_tok = 0, sorted_slot = 0, sorted_w = 0, logits = 0, h = 0, slots = 0, acc = 0,
-         total = 0;
+         num_work = 0, sorted_tok = 0, sorted_slot = 0, sorted_w = 0, logits = 0, stats_part = 0, h = 0, slots = 0,
+         acc = 0, total = 0;
 };
 
 int elem_bytes(int32_t dt) { return dt == MOE_BF16 ? 2 : 4; }
@@ -100,6 +101,7 @@ Layout layout_of(const moe_desc* d) {
   L.sorted_slot = take(sizeof(int32_t) * M);
   L.sorted_w = take(sizeof(float) * M);
   L.logits = take(sizeof(float) * T * E);
+  L.stats_part = take(sizeof(float) * (size_t)router_blocks(T) * 3 * E);
   L.h = take((size_t)elem_bytes(d->dtype) * M * F);
   if (d->deterministic) L.slots = take(sizeof(float) * M * D);
   if (!d->deterministic && d->out_dtype == MOE_BF16) L.acc = take(sizeof(float) * T * D);
@@ -108,6 +110,52 @@ Layout layout_of(const moe_desc* d) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Routing options resolved on the host.
+struct RoutePlan {
+  const int64_t* replay = nullptr;
+  const uint8_t* replay_mask = nullptr;
+  float threshold = 0.f;
+  bool capacity = false;  // drops for capacity are possible
+  int64_t seq_len = 0;
+  int32_t slots = 0;
+  uint8_t* kept = nullptr;
+  float* stats = nullptr;
+  bool drops() const { return threshold > 0.f || capacity; }
+};
+
+moe_status plan_routing(const moe_desc* d, const moe_routing* r, RoutePlan* out) {
+  RoutePlan p;
+  if (r) {
+    if (!(r->dynamic_threshold >= 0.f) || !(r->capacity_factor >= 0.0) || r->seq_len < 0) return MOE_EINVAL;
+    if (r->dynamic_threshold > 0.f && !d->norm_topk) return MOE_EINVAL;
+    p.replay = r->replay_experts;
+    p.replay_mask = r->replay_experts ? r->replay_mask : nullptr;
+    p.threshold = r->dynamic_threshold;
+    p.kept = r->kept;
+    p.stats = r->stats;
+    if (r->capacity_factor > 0.0) {
+      const int64_t L = r->seq_len ? r->seq_len : d->T;
+      if (L > 0 && d->T % L != 0) return MOE_EINVAL;
+      if (L > 0) {
+        // the Dew page, section "Expert computation and placement":
+        // max(ceil(L*K/E) * cf, cf) slots, rounded down to whole slots
+        const double base = (double)((L * d->K + d->E - 1) / d->E);
+        double c = base * r->capacity_factor;
+        if (c < r->capacity_factor) c = r->capacity_factor;
+        c = floor(c);
+        // a sequence holds L*K assignments: more slots than that drop nothing
+        if (c < (double)(L * d->K)) {
+          p.capacity = true;
+          p.seq_len = L;
+          p.slots = (int32_t)c;
+        }
+      }
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
 
 template <typename T>
 T* at(void* ws, size_t off) {
@@ -125,7 +173,7 @@ struct Marks {
   }
 };
 
-moe_status route_and_sort(const moe_desc* d, const Layout& L, const void* x, const void* router,
+moe_status route_and_sort(const moe_desc* d, const RoutePlan& rp, const Layout& L, const void* x, const void* router,
                           const float* router_bias, int64_t* sel, float* weights, float* logits,
                           int32_t* counts_out, int32_t* offsets_out, int32_t* sorted_tok, int32_t* sorted_slot,
                           float* zero_rows, void* ws, hipStream_t s, const Marks& mk, bool build_work) {
@@ -146,7 +194,22 @@ moe_status route_and_sort(const moe_desc* d, const Layout& L, const void* x, con
   ra.zero_rows = zero_rows;
   ra.zero_cols = d->D;
   ra.vec_ok = aligned16(x) && aligned16(router) && ((d->D * eb) % 16 == 0);
-  if (launch_router(d->dtype, ra, s) != hipSuccess || !mk.mark(1)) return MOE_EDEVICE;
+  ra.replay = rp.replay;
+  ra.replay_mask = rp.replay_mask;
+  ra.threshold = rp.threshold;
+  ra.kept = rp.kept;
+  ra.stats_part = rp.stats ? at<float>(ws, L.stats_part) : nullptr;
+  if (launch_router(d->dtype, ra, s) != hipSuccess) return MOE_EDEVICE;
+  if (rp.stats) {
+    StatsArgs sa{};
+    sa.part = ra.stats_part;
+    sa.blocks = router_blocks(d->T);
+    sa.T = d->T;
+    sa.E = d->E;
+    sa.stats = rp.stats;
+    if (launch_stats(sa, s) != hipSuccess) return MOE_EDEVICE;
+  }
+  if (!mk.mark(1)) return MOE_EDEVICE;
 
   DispatchArgs da{};
   da.sel32 = ra.sel32;
@@ -174,11 +237,31 @@ moe_status route_and_sort(const moe_desc* d, const Layout& L, const void* x, con
     da.spec[i].work = at<int2>(ws, works[i]);
     da.spec[i].num_work = at<int32_t>(ws, L.num_work) + i;
   }
+  if (rp.capacity) {
+    // Sort the (threshold-kept) assignments once, drop the slots past each
+    // sequence's capacity, then sort the survivors for the GEMMs.
+    DispatchArgs first = da;
+    first.counts_out = nullptr;
+    first.offsets_out = nullptr;
+    first.nspec = 0;
+    if (launch_dispatch(first, s) != hipSuccess) return MOE_EDEVICE;
+    CapacityArgs ca{};
+    ca.offsets = da.offsets;
+    ca.sorted_tok = da.sorted_tok;
+    ca.sorted_slot = da.sorted_slot;
+    ca.sel32 = ra.sel32;
+    ca.kept = rp.kept;
+    ca.M = L.M;
+    ca.seq_len = rp.seq_len;
+    ca.E = d->E;
+    ca.slots = rp.slots;
+    if (launch_capacity(ca, s) != hipSuccess) return MOE_EDEVICE;
+  }
   if (launch_dispatch(da, s) != hipSuccess || !mk.mark(2)) return MOE_EDEVICE;
   return MOE_OK;
 }
 
-moe_status forward_impl(const moe_desc* d, const void* x, const void* router, const void* gate_up_proj,
+moe_status forward_impl(const moe_desc* d, const moe_routing* r, const void* x, const void* router, const void* gate_up_proj,
                         const void* down_proj, const float* router_bias, const float* up_bias,
                         const float* down_bias, void* out, int64_t* selected_experts, float* routing_weights,
                         float* router_logits, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
@@ -188,6 +271,9 @@ moe_status forward_impl(const moe_desc* d, const void* x, const void* router, co
   if (d->T == 0) return MOE_OK;
   if (!x || !router || !gate_up_proj || !down_proj || !out || !selected_experts || !routing_weights || !workspace)
     return MOE_EINVAL;
+  RoutePlan rp;
+  st = plan_routing(d, r, &rp);
+  if (st != MOE_OK) return st;
   const Layout L = layout_of(d);
   if (workspace_bytes < L.total) return MOE_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -201,8 +287,8 @@ moe_status forward_impl(const moe_desc* d, const void* x, const void* router, co
   if (!d->deterministic) acc = d->out_dtype == MOE_F32 ? static_cast<float*>(out) : at<float>(workspace, L.acc);
 
   if (!mk.mark(0)) return MOE_EDEVICE;
-  st = route_and_sort(d, L, x, router, router_bias, selected_experts, routing_weights, router_logits, expert_counts,
-                      nullptr, nullptr, nullptr, acc, workspace, s, mk, true);
+  st = route_and_sort(d, rp, L, x, router, router_bias, selected_experts, routing_weights, router_logits,
+                      expert_counts, nullptr, nullptr, nullptr, acc, workspace, s, mk, true);
   if (st != MOE_OK) return st;
 
   GemmArgs g{};
@@ -262,10 +348,36 @@ moe_status forward_impl(const moe_desc* d, const void* x, const void* router, co
     f.D = d->D;
     f.K = d->deterministic ? d->K : 1;
     f.out_bf16 = d->out_dtype == MOE_BF16;
+    if (d->deterministic && rp.drops()) {  // dropped slots have no row: skip them
+      f.slot_expert = at<int32_t>(workspace, L.sel32);
+      f.E = d->E;
+    }
     if (launch_finalize(f, s) != hipSuccess) return MOE_EDEVICE;
   }
   if (!mk.mark(5)) return MOE_EDEVICE;
   return MOE_OK;
+}
+
+moe_status dispatch_impl(const moe_desc* d, const moe_routing* r, const void* x, const void* router,
+                         const float* router_bias, int64_t* selected_experts, float* routing_weights,
+                         float* router_logits, int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* sorted_token, int32_t* sorted_slot, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!x || !router || !selected_experts || !routing_weights || !expert_counts || !expert_offsets ||
+      !sorted_token || !sorted_slot || !workspace)
+    return MOE_EINVAL;
+  RoutePlan rp;
+  st = plan_routing(d, r, &rp);
+  if (st != MOE_OK) return st;
+  const Layout L = layout_of(d);
+  if (workspace_bytes < L.total) return MOE_EWORKSPACE;
+  const Marks none{nullptr, 0, nullptr};
+  return route_and_sort(d, rp, L, x, router, router_bias, selected_experts, routing_weights, router_logits,
+                        expert_counts, expert_offsets, sorted_token, sorted_slot, nullptr, workspace,
+                        static_cast<hipStream_t>(stream), none, false);
 }
 
 }  // namespace
@@ -299,8 +411,19 @@ moe_status moe_forward(const moe_desc* d, const void* x, const void* router, con
                        const float* down_bias, void* out, int64_t* selected_experts, float* routing_weights,
                        float* router_logits, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  return forward_impl(d, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out, selected_experts,
-                      routing_weights, router_logits, expert_counts, workspace, workspace_bytes, stream, nullptr, 0);
+  return forward_impl(d, nullptr, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out,
+                      selected_experts, routing_weights, router_logits, expert_counts, workspace, workspace_bytes,
+                      stream, nullptr, 0);
+}
+
+moe_status moe_forward_routed(const moe_desc* d, const moe_routing* r, const void* x, const void* router,
+                              const void* gate_up_proj, const void* down_proj, const float* router_bias,
+                              const float* up_bias, const float* down_bias, void* out, int64_t* selected_experts,
+                              float* routing_weights, float* router_logits, int32_t* expert_counts,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(d, r, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out,
+                      selected_experts, routing_weights, router_logits, expert_counts, workspace, workspace_bytes,
+                      stream, nullptr, 0);
 }
 
 moe_status moe_forward_timed(const moe_desc* d, const void* x, const void* router, const void* gate_up_proj,
@@ -309,27 +432,26 @@ moe_status moe_forward_timed(const moe_desc* d, const void* x, const void* route
                              float* routing_weights, float* router_logits, int32_t* expert_counts,
                              void* workspace, size_t workspace_bytes, void* stream, void* const* events,
                              int32_t n_events) {
-  return forward_impl(d, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out, selected_experts,
-                      routing_weights, router_logits, expert_counts, workspace, workspace_bytes, stream, events,
-                      n_events);
+  return forward_impl(d, nullptr, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out,
+                      selected_experts, routing_weights, router_logits, expert_counts, workspace, workspace_bytes,
+                      stream, events, n_events);
 }
 
 moe_status moe_dispatch(const moe_desc* d, const void* x, const void* router, const float* router_bias,
                         int64_t* selected_experts, float* routing_weights, float* router_logits,
                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_token,
                         int32_t* sorted_slot, void* workspace, size_t workspace_bytes, void* stream) {
-  moe_status st = check_desc(d);
-  if (st != MOE_OK) return st;
-  if (d->T == 0) return MOE_OK;
-  if (!x || !router || !selected_experts || !routing_weights || !expert_counts || !expert_offsets ||
-      !sorted_token || !sorted_slot || !workspace)
-    return MOE_EINVAL;
-  const Layout L = layout_of(d);
-  if (workspace_bytes < L.total) return MOE_EWORKSPACE;
-  const Marks none{nullptr, 0, nullptr};
-  return route_and_sort(d, L, x, router, router_bias, selected_experts, routing_weights, router_logits,
-                        expert_counts, expert_offsets, sorted_token, sorted_slot, nullptr, workspace,
-                        static_cast<hipStream_t>(stream), none, false);
+  return dispatch_impl(d, nullptr, x, router, router_bias, selected_experts, routing_weights, router_logits,
+                       expert_counts, expert_offsets, sorted_token, sorted_slot, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_dispatch_routed(const moe_desc* d, const moe_routing* r, const void* x, const void* router,
+                               const float* router_bias, int64_t* selected_experts, float* routing_weights,
+                               float* router_logits, int32_t* expert_counts, int32_t* expert_offsets,
+                               int32_t* sorted_token, int32_t* sorted_slot, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return dispatch_impl(d, r, x, router, router_bias, selected_experts, routing_weights, router_logits,
+                       expert_counts, expert_offsets, sorted_token, sorted_slot, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -54,8 +54,42 @@ struct RouterArgs {
   float* zero_rows;   // (T,zero_cols) rows cleared by this kernel, or null
   int64_t zero_cols;
   int32_t vec_ok;     // x and router rows 16-byte aligned: vector loads allowed
+  // Routing options (all off when null / 0).
+  const int64_t* replay;        // (T,K) recorded experts, or null
+  const uint8_t* replay_mask;   // (T) nonzero: the record covers the token; null: all covered
+  float threshold;              // dynamic threshold on renormalised weights, 0 = off
+  uint8_t* kept;                // (T,K) 1/0 out, or null
+  float* stats_part;            // (blocks, 3E) per-block sums of p, gate, [gate > 0], or null
 };
 hipError_t launch_router(int dtype, const RouterArgs& a, hipStream_t s);
+inline int64_t router_blocks(int64_t T) { return (T + kRouterTokens - 1) / kRouterTokens; }
+
+// Balancing statistics from the router's per-block sums: stats (3E + 4) =
+// mean p (E), mean gate (E), mean [gate > 0] (E), switch, gshard, master,
+// gshard_probs.
+struct StatsArgs {
+  const float* part;  // (blocks, 3E)
+  int64_t blocks, T;
+  int32_t E;
+  float* stats;       // (3E + 4)
+};
+hipError_t launch_stats(const StatsArgs& a, hipStream_t s);
+
+// Capacity drops on a stable expert-sorted order: a sorted row whose rank
+// among its expert's rows from the same sequence is >= slots is dropped: its
+// assignment's expert becomes the sentinel E and its kept flag 0.
+struct CapacityArgs {
+  const int32_t* offsets;     // (E+1) of the sorted order
+  const int32_t* sorted_tok;  // (M)
+  const int32_t* sorted_slot; // (M)
+  int32_t* sel32;             // (M) by assignment, updated
+  uint8_t* kept;              // (M) by assignment, or null
+  int64_t M;
+  int64_t seq_len;
+  int32_t E;
+  int32_t slots;
+};
+hipError_t launch_capacity(const CapacityArgs& a, hipStream_t s);
 
 // A grouped GEMM's work list: item b is one (expert, row tile, column tile).
 // Items are ordered so that consecutive items share operands (all row tiles of
@@ -72,7 +106,7 @@ struct WorkSpec {
 constexpr int kColGroup = 4;  // column tiles per ordering group
 
 struct DispatchArgs {
-  const int32_t* sel32;   // (M) expert of assignment i = t*K + k
+  const int32_t* sel32;   // (M) expert of assignment i = t*K + k; E = dropped
   const float* weights;   // (M)
   int64_t M;
   int32_t E, K;
@@ -135,6 +169,8 @@ struct FinalizeArgs {
   int64_t T, D;
   int32_t K;          // slots per token to sum (1 = plain copy/cast)
   int32_t out_bf16;
+  const int32_t* slot_expert;  // (T*K) or null: slots whose entry is >= E were dropped and are skipped
+  int32_t E;
 };
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
 

@@ -163,6 +163,13 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
   }
   __syncthreads();
 
+  // Regions of `part` free after the sum above: p (16 x EP), and the
+  // weights and experts of the 16 tokens' K slots (16 x K, K <= EP), read
+  // by the per-block statistics.
+  float* pbuf = part + 16 * EP;
+  float* wbuf = part + 32 * EP;
+  int* sbuf = reinterpret_cast<int*>(part + 48 * EP);
+
   // Softmax and top-k with L lanes per token.
   int L = 1;
   while (L < E && L < 64) L <<= 1;
@@ -192,11 +199,31 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
     }
     for (int o = L >> 1; o > 0; o >>= 1) s += __shfl_xor(s, o);
 
+    float pr[4];
     uint64_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = j + i * L;
-      key[i] = (e < E) ? (((uint64_t)__float_as_uint(ev[i] / s) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
+      pr[i] = ev[i] / s;
+      key[i] = (e < E) ? (((uint64_t)__float_as_uint(pr[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
+    }
+    const int64_t t = t0 + tk;
+
+    // Routing replay (the Dew "Mixture of experts" page, section "Router
+    // behavior"): a token the record covers takes the recorded experts, with
+    // this forward's probabilities.  A record holding an index outside
+    // [0, E) does not cover its token.  `covered` is uniform in the group.
+    bool covered = false;
+    if (a.replay) {
+      int bad = 0;
+      if (active) {
+        for (int k = j; k < K; k += L) {
+          const int64_t e = a.replay[t * K + k];
+          bad |= (e < 0 || e >= E) ? 1 : 0;
+        }
+      }
+      for (int o = L >> 1; o > 0; o >>= 1) bad |= __shfl_xor(bad, o);
+      covered = active && !bad && (!a.replay_mask || a.replay_mask[t] != 0);
     }
 
     float psum = 0.f;
@@ -210,14 +237,25 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
         const uint64_t other = shfl_xor_u64(best, o);
         best = other > best ? other : best;
       }
-      const int e = (int)(0xffffffffu - (uint32_t)best);
-      const float p = __uint_as_float((uint32_t)(best >> 32));
-      psum += p;
+      int e = (int)(0xffffffffu - (uint32_t)best);
+      float p = __uint_as_float((uint32_t)(best >> 32));
       if (e % L == j) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (e / L == i) key[i] = 0ull;
       }
+      if (a.replay) {
+        // p of the recorded expert: lane (e % L) of the group holds it as pr[e / L]
+        const int er = covered ? (int)a.replay[t * K + k] : 0;
+        const int q = er / L;
+        const float mine = q == 0 ? pr[0] : (q == 1 ? pr[1] : (q == 2 ? pr[2] : pr[3]));
+        const float pe = __shfl(mine, (lane & ~(L - 1)) | (er & (L - 1)));
+        if (covered) {
+          e = er;
+          p = pe;
+        }
+      }
+      psum += p;
       const int kq = k / L, kr = k % L;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -226,19 +264,118 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
           myp[i] = p;
         }
     }
+
+    // Weights; the dynamic threshold (the ES-MoE "API" page, settings table
+    // of "ESMoE"): a non-leading slot whose renormalised weight is below the
+    // threshold is dropped and the kept weights are renormalised.
+    const float denom = psum + 1e-9f;
+    float wk[4];
+    bool keep[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = j + i * L;
+      wk[i] = a.norm ? myp[i] / denom : myp[i];
+      keep[i] = k < K;
+    }
+    if (a.threshold > 0.f) {
+      float ks = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = j + i * L;
+        if (k > 0 && wk[i] < a.threshold) keep[i] = false;
+        if (keep[i]) ks += wk[i];
+      }
+      for (int o = L >> 1; o > 0; o >>= 1) ks += __shfl_xor(ks, o);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wk[i] = keep[i] ? wk[i] / ks : 0.f;
+    }
+
     if (active) {
-      const float denom = psum + 1e-9f;
-      const int64_t t = t0 + tk;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k = j + i * L;
         if (k < K) {
           a.sel64[t * K + k] = mysel[i];
-          a.sel32[t * K + k] = mysel[i];
-          a.weights[t * K + k] = a.norm ? myp[i] / denom : myp[i];
+          a.sel32[t * K + k] = keep[i] ? mysel[i] : E;  // E: dropped, takes no row
+          a.weights[t * K + k] = wk[i];
+          if (a.kept) a.kept[t * K + k] = keep[i] ? 1 : 0;
+          if (a.stats_part) {
+            wbuf[tk * EP + k] = wk[i];
+            sbuf[tk * EP + k] = mysel[i];
+          }
+        }
+      }
+      if (a.stats_part) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = j + i * L;
+          if (e < E) pbuf[tk * EP + e] = pr[i];
         }
       }
     }
+  }
+
+  // Per-block sums for the balancing statistics, in a fixed order: for each
+  // expert, the sum over this block's tokens of p, of the gate (the token's
+  // weights at that expert) and of [gate > 0].
+  if (a.stats_part) {
+    __syncthreads();
+    const int nt = (int)min((int64_t)kRouterTokens, a.T - t0);
+    float* dst = a.stats_part + (int64_t)blockIdx.x * 3 * E;
+    for (int e = tid; e < E; e += kThreads) {
+      float sp = 0.f, sg = 0.f, sc = 0.f;
+      for (int tk = 0; tk < nt; ++tk) {
+        sp += pbuf[tk * EP + e];
+        float g = 0.f;
+        for (int k = 0; k < K; ++k) g += sbuf[tk * EP + k] == e ? wbuf[tk * EP + k] : 0.f;
+        sg += g;
+        sc += g > 0.f ? 1.f : 0.f;
+      }
+      dst[e] = sp;
+      dst[E + e] = sg;
+      dst[2 * E + e] = sc;
+    }
+  }
+}
+
+// Balancing objectives (the ES-MoE "API" page, section "Balancing
+// objectives") from the router's per-block sums.  One block: wave w sums the
+// columns c = w, w+4, ... over the blocks with a fixed lane split and a fixed
+// shuffle tree (reproducible), then one thread forms the four objectives in
+// double precision from the E means.
+__global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
+  __shared__ float mean[3 * kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int E = a.E, C = 3 * E;
+  for (int c = w; c < C; c += kThreads / 64) {
+    float v = 0.f;
+    for (int64_t b = lane; b < a.blocks; b += 64) v += a.part[b * C + c];
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) {
+      mean[c] = v / (float)a.T;
+      a.stats[c] = mean[c];
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double sp = 0.0, sg = 0.0, sw = 0.0;
+    for (int e = 0; e < E; ++e) {
+      sp += mean[e];
+      sg += mean[E + e];
+      sw += (double)mean[e] * mean[2 * E + e];
+    }
+    double gs = 0.0, ms = 0.0, ps = 0.0;
+    for (int e = 0; e < E; ++e) {
+      const double ug = sg > 0.0 ? mean[E + e] / sg : 0.0;
+      const double up = sp > 0.0 ? mean[e] / sp : 0.0;
+      gs += ug * ug;
+      ms += (ug - 1.0 / E) * (ug - 1.0 / E);
+      ps += up * up;
+    }
+    a.stats[C + 0] = (float)(E * sw);   // switch
+    a.stats[C + 1] = (float)(E * gs);   // gshard
+    a.stats[C + 2] = (float)(ms / E);   // master
+    a.stats[C + 3] = (float)(E * ps);   // gshard_probs
   }
 }
 
@@ -265,6 +402,12 @@ hipError_t launch_tag(const RouterArgs& a, hipStream_t s) {
 hipError_t launch_router(int dtype, const RouterArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   return dtype == 1 ? launch_tag<BF16>(a, s) : launch_tag<F32>(a, s);
+}
+
+hipError_t launch_stats(const StatsArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -28,8 +28,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("moe_forward", "moe_forward_timed", "moe_dispatch", "moe_workspace_bytes", "moe_status_string",
-              "moe_abi_version"):
+    for n in ("moe_forward", "moe_forward_timed", "moe_forward_routed", "moe_dispatch", "moe_dispatch_routed",
+              "moe_workspace_bytes", "moe_status_string", "moe_abi_version"):
         assert n in names
 
 
@@ -47,8 +47,17 @@ def test_desc_layout_matches_header():
     assert moe.MoeDesc.E.offset == 24 and moe.MoeDesc.deterministic.offset == 48
 
 
+def test_routing_layout_matches_header():
+    # two pointers, float (padded), double, int64, two pointers
+    R = moe.MoeRouting
+    assert ctypes.sizeof(R) == 56
+    assert (R.replay_experts.offset, R.replay_mask.offset, R.dynamic_threshold.offset, R.capacity_factor.offset,
+            R.seq_len.offset, R.kept.offset, R.stats.offset) == (0, 8, 16, 24, 32, 40, 48)
+    assert moe.stats_len(8) == 28
+
+
 def test_abi_version_and_strings(lib):
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
     for code in range(6):
         assert len(moe.moe_status_string(code)) > 0
     assert moe.moe_status_string(99) == "unknown status"
@@ -76,6 +85,34 @@ def test_validation_codes(lib, kw, code):
                            1 << 40, None) == code
     assert moe.moe_dispatch(d, fake, fake, None, fake, fake, None, fake, fake, fake, fake, fake, 1 << 40,
                             None) == code
+
+
+@pytest.mark.parametrize("desc_kw,rkw", [
+    (dict(), dict(dynamic_threshold=-0.1)),
+    (dict(), dict(dynamic_threshold=float("nan"))),
+    (dict(norm_topk=0), dict(dynamic_threshold=0.2)),
+    (dict(), dict(capacity_factor=-1.0)),
+    (dict(), dict(capacity_factor=float("nan"))),
+    (dict(), dict(capacity_factor=1.0, seq_len=5)),   # 5 does not divide T = 16
+    (dict(), dict(seq_len=-4)),
+])
+def test_routing_validation(lib, desc_kw, rkw):
+    d = _desc(**desc_kw)
+    r = moe.MoeRouting(**rkw)
+    fake = 16
+    assert moe.moe_forward_routed(d, r, fake, fake, fake, fake, None, None, None, fake, fake, fake, None, None, fake,
+                                  1 << 40, None) == moe.MOE_EINVAL
+    assert moe.moe_dispatch_routed(d, r, fake, fake, None, fake, fake, None, fake, fake, fake, fake, fake, 1 << 40,
+                                   None) == moe.MOE_EINVAL
+
+
+def test_routing_options_off_is_plain_forward(lib):
+    # a NULL routing pointer and an all-zero struct validate like moe_forward
+    d = _desc(K=0)
+    fake = 16
+    for r in (None, moe.MoeRouting()):
+        assert moe.moe_forward_routed(d, r, fake, fake, fake, fake, None, None, None, fake, fake, fake, None, None,
+                                      fake, 1 << 40, None) == moe.MOE_EINVAL
 
 
 def test_missing_pointers_and_small_workspace(lib):
