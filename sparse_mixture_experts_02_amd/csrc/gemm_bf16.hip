@@ -18,9 +18,11 @@
 // swizzle, while XOR-ing with the low row bits halves its throughput
 // (measured with a probe of the two patterns).  A lane of a load instruction writes LDS byte 16*lane of a
 // block of 1024/KB rows, so it loads the global chunk the swizzle puts there.
-// The loads of a stage are issued S-1 steps before it is consumed; one
-// barrier per step, waited on only for the loads of the stage being
-// published (s_waitcnt vmcnt with the later stages left in flight).
+// The 8-wave prefill tile runs a ping-pong schedule (two wave groups take
+// turns between matrix-core work and LDS/global traffic, four barriers per
+// stage, loads issued a stage ahead); the other shapes issue the loads of a
+// stage S-1 steps before it is consumed with one barrier per step, waited on
+// only for the loads of the stage being published.
 //
 // Requires K % 64 == 0, 16-byte aligned operands, and operand regions under
 // 4 GiB (32-bit byte offsets); the host routes anything else to the generic
@@ -171,12 +173,6 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) co[t] = ((2 * t + h) ^ swz(l32)) * 16;  // row bases are multiples of 32
 
-  // One K step from one LDS stage = NT 16-k slices.  A "group" is the NB
-  // MFMAs of one A fragment (NB*32 cycles of matrix core work).  Every LDS
-  // read is issued at least one group before its use: the next A fragment one
-  // group ahead, the next slice's B fragments spread over the current slice's
-  // groups.  Only the first slice's first reads wait on LDS, once per stage.
-  // Scheduling barriers keep this order.
   constexpr int NB = NACC * SN;
   auto rdA = [&](const char* buf, int t, int mi) {
     return *reinterpret_cast<const bf16x8*>(buf + (arow + mi * 32) * KB + co[t]);
@@ -184,51 +180,139 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   auto rdB = [&](const char* buf, int t, int j) {
     return *reinterpret_cast<const bf16x8*>(buf + AB + ((j / SN) * OUTC + brow + (j % SN) * 32) * KB + co[t]);
   };
-  auto compute = [&](const char* buf) {
-    bf16x8 fb[2][NB], fa[2];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) fb[0][j] = rdB(buf, 0, j);
-    fa[0] = rdA(buf, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int mi = 0; mi < SM; ++mi) {
-        const int g = t * SM + mi;  // group index in the stage
-        if (mi + 1 < SM)
-          fa[(g + 1) & 1] = rdA(buf, t, mi + 1);
-        else if (t + 1 < NT)
-          fa[(g + 1) & 1] = rdA(buf, t + 1, 0);
-        if (t + 1 < NT) {
-#pragma unroll
-          for (int j = mi * NB / SM; j < (mi + 1) * NB / SM; ++j) fb[(t + 1) & 1][j] = rdB(buf, t + 1, j);
-        }
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[j / SN][mi][j % SN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[t & 1][j], fa[g & 1],
-                                                                          acc[j / SN][mi][j % SN], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-
-  // Step kt: wait for this wave's loads of stage kt (the S-2 later stages
-  // stay in flight), barrier (stage kt visible to all waves; all waves done
-  // with stage kt-1), issue stage kt+S-1 into the buffer of stage kt-1, then
-  // the MFMAs of stage kt.
   // A wave whose rows all lie past the end of the expert's segment (the last
-  // row tile of an expert is usually partial) skips its MFMAs; it still loads
-  // and meets every barrier.
+  // row tile of an expert is usually partial) skips its MFMAs and fragment
+  // reads; it still loads its share of every stage and meets every barrier.
   const bool busy = wm * WM < rows;
+  if constexpr (S == 2 && NW == 8 && NT == 4) {
+    // Ping-pong schedule of the 8-wave tile.  Waves 0-3 (group 0) and 4-7
+    // (group 1) put one wave of each group on every SIMD.  Time is cut into
+    // phases of half a stage (two 16-k slices); in every phase one group
+    // issues the 16 MFMAs of a half stage from fragments already in
+    // registers while the other group reads the fragments of its next half
+    // stage from LDS (and, in its first phase of a stage, issues its loads of
+    // the next stage), so the matrix core of a SIMD always has a wave with
+    // work and LDS latency is never exposed to it.  Group 1 runs one phase
+    // behind group 0.  Every phase ends with a workgroup barrier.
+    //   stage k, phase 0: g0 loads k+1, reads half 0  | g1 computes half 1 of k-1
+    //            phase 1: g0 computes half 0          | g1 loads k+1, reads half 0
+    //            phase 2: g0 reads half 1             | g1 computes half 0
+    //            phase 3: g0 computes half 1          | g1 reads half 1; all wait
+    //                     for their loads of stage k+1 before the barrier
+    // Stage k's buffer is last read in phase 3 of stage k, so the loads of
+    // stage k+2 into it (issued in phase 0/1 of stage k+1) follow a barrier.
+    const int grp = w >> 2;
+    bf16x8 fa[2][SM], fb[2][NB];
+    auto memread = [&](const char* buf, int hs) {
+      if (!busy) return;
 #pragma unroll
-  for (int p = 0; p < S - 1; ++p) issue(p);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vm<(S - 2) * NI>();
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) fb[u][j] = rdB(buf, 2 * hs + u, j);
+#pragma unroll
+        for (int mi = 0; mi < SM; ++mi) fa[u][mi] = rdA(buf, 2 * hs + u, mi);
+      }
+    };
+    auto mma = [&]() {
+      if (!busy) return;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int mi = 0; mi < SM; ++mi)
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            acc[j / SN][mi][j % SN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[u][j], fa[u][mi],
+                                                                            acc[j / SN][mi][j % SN], 0, 0, 0);
+    };
+    auto phase_end = [&](bool loads) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's fragment reads have landed
+      if (loads) wait_vm<0>();
+      barrier_lds();
+    };
+    issue(0);
+    wait_vm<0>();
     barrier_lds();
-    issue(kt + S - 1);
-    if (busy) compute(lds + (kt % S) * STAGE);
+    // The two groups run separate straight-line loops (a branch-free body
+    // keeps the fragments in registers); both meet the same barriers.
+    if (grp == 0) {
+      for (int k = 0; k < nk; ++k) {
+        const char* buf = lds + (k & 1) * STAGE;
+        if (k + 1 < nk) issue(k + 1);
+        memread(buf, 0);
+        phase_end(false);
+        mma();
+        phase_end(false);
+        memread(buf, 1);
+        phase_end(false);
+        mma();
+        phase_end(true);
+      }
+    } else {
+      for (int k = 0; k < nk; ++k) {
+        const char* buf = lds + (k & 1) * STAGE;
+        if (k > 0) mma();
+        phase_end(false);
+        if (k + 1 < nk) issue(k + 1);
+        memread(buf, 0);
+        phase_end(false);
+        mma();
+        phase_end(false);
+        memread(buf, 1);
+        phase_end(true);
+      }
+      mma();
+    }
+    wait_vm<0>();  // no LDS DMA may outlive the workgroup
+  } else {
+    // Other shapes: every wave loads, waits and computes each stage in step.
+    // One K step from one LDS stage = NT 16-k slices.  A "group" is the NB
+    // MFMAs of one A fragment (NB*32 cycles of matrix core work).  Every LDS
+    // read is issued at least one group before its use: the next A fragment
+    // one group ahead, the next slice's B fragments spread over the current
+    // slice's groups.  Only the first slice's first reads wait on LDS, once
+    // per stage.  Scheduling barriers keep this order.
+    // Step kt: wait for this wave's loads of stage kt (the S-2 later stages
+    // stay in flight), barrier (stage kt visible to all waves; all waves done
+    // with stage kt-1), issue stage kt+S-1 into the buffer of stage kt-1,
+    // then the MFMAs of stage kt.
+    auto compute = [&](const char* buf) {
+      bf16x8 fb[2][NB], fa[2];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) fb[0][j] = rdB(buf, 0, j);
+      fa[0] = rdA(buf, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int mi = 0; mi < SM; ++mi) {
+          const int g = t * SM + mi;  // group index in the stage
+          if (mi + 1 < SM)
+            fa[(g + 1) & 1] = rdA(buf, t, mi + 1);
+          else if (t + 1 < NT)
+            fa[(g + 1) & 1] = rdA(buf, t + 1, 0);
+          if (t + 1 < NT) {
+#pragma unroll
+            for (int j = mi * NB / SM; j < (mi + 1) * NB / SM; ++j) fb[(t + 1) & 1][j] = rdB(buf, t + 1, j);
+          }
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            acc[j / SN][mi][j % SN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[t & 1][j], fa[g & 1],
+                                                                            acc[j / SN][mi][j % SN], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p) issue(p);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vm<(S - 2) * NI>();
+      barrier_lds();
+      issue(kt + S - 1);
+      if (busy) compute(lds + (kt % S) * STAGE);
+    }
+    wait_vm<0>();  // no LDS DMA may outlive the workgroup
   }
-  wait_vm<0>();  // no LDS DMA may outlive the workgroup
 
   const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;
 #pragma unroll
