@@ -131,9 +131,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DispatchArgs a) {
     __syncthreads();
     const int ntn = sp.ntn;
     const int total = tiles * ntn;
-    if (tid == 0) sp.num_work[0] = total;
-    for (int b = tid; b < total && b < sp.max_work; b += kScanThreads) {
-      const int L = xcd_order(b, total);
+    // The item at position L of the order.
+    auto item = [&](int L) {
       // expert: the last x with tst[x] * ntn <= L
       int lo = 0, hi = E;
       while (hi - lo > 1) {
@@ -155,8 +154,30 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DispatchArgs a) {
         n = (ntn / kColGroup) * kColGroup + r / mt;
         m = r % mt;
       }
-      sp.work[b] = make_int2(x | (n << 8), offs[x] + m * sp.bm);
+      return make_int2(x | (n << 8), offs[x] + m * sp.bm);
+    };
+    // Items past the last full round of split_ncu blocks are cut along K.
+    int R = 0, P = 1;
+    if (sp.split_ncu > 0 && total > 0) {
+      R = total % sp.split_ncu;
+      P = R > 0 ? min(4, sp.split_ncu / R) : 1;
+      if (P < 2) R = 0, P = 1;
     }
+    const int F = total - R;
+    const int n_items = F + R * P;
+    if (tid == 0) {
+      sp.num_work[0] = n_items;
+      if (sp.split_info) {
+        sp.split_info[0] = R;
+        sp.split_info[1] = P;
+      }
+    }
+    for (int j = tid; j < R; j += kScanThreads) sp.split_tiles[j] = item(F + j);
+    // Blocks [0, F) take the full items in the XCD order; blocks [F, F+R*P)
+    // the split parts, which blocks b % 8 spread evenly over the XCDs and
+    // which dispatch last.
+    for (int b = tid; b < n_items && b < sp.max_work; b += kScanThreads)
+      sp.work[b] = b < F ? item(xcd_order(b, F)) : make_int2(kSplitItem | (b - F), 0);
   }
 }
 

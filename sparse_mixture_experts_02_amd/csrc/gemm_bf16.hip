@@ -96,7 +96,23 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
 
   if ((int)blockIdx.x >= a.num_work[0]) return;
-  const int2 wk = a.work[blockIdx.x];
+  // K steps of KB/2 elements; a split item covers steps [kb0, ke0) of its
+  // tile and leaves its fp32 partial sums for launch_split_fixup.
+  const int nk = (int)(a.Kd / (KB / 2));
+  constexpr bool SPLITTABLE = EPI == EPI_DOWN_SLOT && S == 2 && NW == 8 && NT == 4;
+  int2 wk = a.work[blockIdx.x];
+  int kb0 = 0, ke0 = nk, split_slot = -1;
+  if constexpr (SPLITTABLE) {
+    if (wk.x < 0) {
+      const int q = wk.x & 0x7fffffff;
+      const int P = a.split_info[1];
+      const int j = q / P, p = q - j * P;
+      wk = a.split_tiles[j];
+      kb0 = p * nk / P;
+      ke0 = (p + 1) * nk / P;
+      split_slot = q;
+    }
+  }
   const int e = wk.x & 0xff;
   const int r0 = wk.y;
   const int rows = min(BM, a.offsets[e + 1] - r0);
@@ -140,7 +156,6 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   // Loads of stage kt into its buffer; past the end of K the last stage is
   // reloaded (into a buffer nobody reads any more), so every step issues the
   // same number of loads and the wait count is one constant.
-  const int nk = (int)(a.Kd / (KB / 2));
   auto issue = [&](int kt) {
     char* dst = lds + (kt % S) * STAGE;
     const uint32_t kb = (uint32_t)min(kt, nk - 1) * (uint32_t)KB;
@@ -229,15 +244,15 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
       if (loads) wait_vm<0>();
       barrier_lds();
     };
-    issue(0);
+    issue(kb0);
     wait_vm<0>();
     barrier_lds();
     // The two groups run separate straight-line loops (a branch-free body
     // keeps the fragments in registers); both meet the same barriers.
     if (grp == 0) {
-      for (int k = 0; k < nk; ++k) {
+      for (int k = kb0; k < ke0; ++k) {
         const char* buf = lds + (k & 1) * STAGE;
-        if (k + 1 < nk) issue(k + 1);
+        if (k + 1 < ke0) issue(k + 1);
         memread(buf, 0);
         phase_end(false);
         mma();
@@ -248,11 +263,11 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         phase_end(true);
       }
     } else {
-      for (int k = 0; k < nk; ++k) {
+      for (int k = kb0; k < ke0; ++k) {
         const char* buf = lds + (k & 1) * STAGE;
-        if (k > 0) mma();
+        if (k > kb0) mma();
         phase_end(false);
-        if (k + 1 < nk) issue(k + 1);
+        if (k + 1 < ke0) issue(k + 1);
         memread(buf, 0);
         phase_end(false);
         mma();
@@ -260,7 +275,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         memread(buf, 1);
         phase_end(true);
       }
-      mma();
+      if (ke0 > kb0) mma();
     }
     wait_vm<0>();  // no LDS DMA may outlive the workgroup
   } else {
@@ -314,6 +329,28 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     wait_vm<0>();  // no LDS DMA may outlive the workgroup
   }
 
+  if constexpr (SPLITTABLE) {
+    if (split_slot >= 0) {
+      // raw fp32 partial sums of this K range, tile-local rows x 256 columns
+      float* dst = a.partial + (int64_t)split_slot * (kSplitTileRows * kSplitTileCols);
+#pragma unroll
+      for (int mi = 0; mi < SM; ++mi) {
+        const int m = wm * WM + mi * 32 + l32;
+        if (m >= rows) continue;
+#pragma unroll
+        for (int ni = 0; ni < SN; ++ni)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x16& c0 = acc[0][mi][ni];
+            const int c = wn * WN + ni * 32 + 8 * q4 + 4 * h;
+            *reinterpret_cast<float4*>(dst + m * kSplitTileCols + c) =
+                float4{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
+          }
+      }
+      return;
+    }
+  }
+
   const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;
 #pragma unroll
   for (int mi = 0; mi < SM; ++mi) {
@@ -330,6 +367,36 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         const f32x4 v1{c1[4 * q4], c1[4 * q4 + 1], c1[4 * q4 + 2], c1[4 * q4 + 3]};
         epilogue4<uint16_t, EPI>(a, rc, n0 + wn * WN + ni * 32 + 8 * q4 + 4 * h, v0, v1, bias);
       }
+  }
+}
+
+// Reduction of the split tiles: block j sums the P partial tiles of split
+// tile j in part order (reproducible) and applies the slot epilogue, the same
+// w * (acc + b2) store as an unsplit tile.
+__global__ __launch_bounds__(256) void split_fixup_kernel(GemmArgs a) {
+  const int R = a.split_info[0], P = a.split_info[1];
+  const int j = blockIdx.x;
+  if (j >= R) return;
+  const int2 wk = a.split_tiles[j];
+  const int e = wk.x & 0xff;
+  const int r0 = wk.y;
+  const int rows = min(kSplitTileRows, a.offsets[e + 1] - r0);
+  const int64_t n0 = (int64_t)(wk.x >> 8) * kSplitTileCols;
+  const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;
+  constexpr int C4 = kSplitTileCols / 4;
+  for (int idx = threadIdx.x; idx < rows * C4; idx += 256) {
+    const int m = idx / C4, c = (idx - m * C4) * 4;
+    f32x4 sum{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < P; ++p) {
+      const float4 v = *reinterpret_cast<const float4*>(
+          a.partial + ((int64_t)(j * P + p) * kSplitTileRows + m) * kSplitTileCols + c);
+      sum[0] += v.x;
+      sum[1] += v.y;
+      sum[2] += v.z;
+      sum[3] += v.w;
+    }
+    const RowCtx rc = row_ctx<EPI_DOWN_SLOT>(a, r0 + m);
+    epilogue4<float, EPI_DOWN_SLOT>(a, rc, n0 + c, sum, sum, bias);
   }
 }
 
@@ -350,6 +417,12 @@ hipError_t launch_rows(int var, const GemmArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_split_fixup(const GemmArgs& a, int32_t ncu, hipStream_t s) {
+  if (ncu <= 0) return hipSuccess;
+  hipLaunchKernelGGL(split_fixup_kernel, dim3(ncu), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_bf16(int epi, int var, const GemmArgs& a, hipStream_t s) {
   switch (epi) {

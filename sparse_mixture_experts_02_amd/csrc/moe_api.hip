@@ -24,10 +24,17 @@ struct GemmPlan {
   int32_t bm = 128, cols = 128, ntn = 0, max_work = 0;
 };
 
+// Compute units the K-split of the down projection's last round is planned
+// for (the split buffers are sized for this many; a part with more CUs plans
+// for this many).
+constexpr int32_t kSplitMaxCU = 256;
+
 struct Layout {
   int64_t M = 0;
   int32_t nchunks = 0;
   GemmPlan g1, g2;
+  bool split2 = false;  // the down projection may cut its last round along K
+  size_t split_tiles = 0, split_info = 0, partial = 0;
   size_t sel32 = 0, chunk_counts = 0, chunk_base = 0, counts = 0, offsets = 0, work1 = 0, work2 = 0,
          num_work = 0, sorted_tok = 0, sorted_slot = 0, sorted_w = 0, logits = 0, stats_part = 0, h = 0, slots = 0,
          acc = 0, total = 0;
@@ -83,6 +90,11 @@ Layout layout_of(const moe_desc* d) {
   L.nchunks = (int32_t)((M + kDispatchChunk - 1) / kDispatchChunk);
   L.g1 = plan_gemm(d, M, F, D, T, G * F * D, swiglu);
   L.g2 = plan_gemm(d, M, D, F, M, D * F, false);
+  // Deterministic mode with 256-row tiles: the down projection's items past
+  // its last full round of CUs are cut along K (fp32 partial tiles, reduced in
+  // part order by a fix-up kernel) so they fill one round of shorter blocks.
+  L.split2 = d->deterministic && L.g2.var == VAR_BF16_M256;
+  if (L.split2) L.g2.max_work += kSplitMaxCU;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -104,12 +116,25 @@ Layout layout_of(const moe_desc* d) {
   L.stats_part = take(sizeof(float) * (size_t)router_blocks(T) * 3 * E);
   L.h = take((size_t)elem_bytes(d->dtype) * M * F);
   if (d->deterministic) L.slots = take(sizeof(float) * M * D);
+  if (L.split2) {
+    L.split_tiles = take(sizeof(int2) * kSplitMaxCU);
+    L.split_info = take(sizeof(int32_t) * 2);
+    L.partial = take(sizeof(float) * (size_t)kSplitMaxCU * kSplitTileRows * kSplitTileCols);
+  }
   if (!d->deterministic && d->out_dtype == MOE_BF16) L.acc = take(sizeof(float) * T * D);
   L.total = off;
   return L;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Compute units of the current device (0 if it cannot be read: no K-split).
+int32_t device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n < kSplitMaxCU ? n : kSplitMaxCU;
+}
 
 // Routing options resolved on the host.
 struct RoutePlan {
@@ -237,6 +262,11 @@ moe_status route_and_sort(const moe_desc* d, const RoutePlan& rp, const Layout& 
     da.spec[i].work = at<int2>(ws, works[i]);
     da.spec[i].num_work = at<int32_t>(ws, L.num_work) + i;
   }
+  if (L.split2 && build_work) {
+    da.spec[1].split_ncu = device_cus();
+    da.spec[1].split_tiles = at<int2>(ws, L.split_tiles);
+    da.spec[1].split_info = at<int32_t>(ws, L.split_info);
+  }
   if (rp.capacity) {
     // Sort the (threshold-kept) assignments once, drop the slots past each
     // sequence's capacity, then sort the survivors for the GEMMs.
@@ -335,10 +365,18 @@ moe_status forward_impl(const moe_desc* d, const moe_routing* r, const void* x, 
   h.num_work = at<int32_t>(workspace, L.num_work) + 1;
   h.max_work = L.g2.max_work;
   h.vec_ok = aligned16(down_proj) && ((d->F * eb) % 16 == 0);
+  int32_t ncu = 0;
+  if (L.split2) {
+    ncu = device_cus();
+    h.split_tiles = at<int2>(workspace, L.split_tiles);
+    h.split_info = at<int32_t>(workspace, L.split_info);
+    h.partial = at<float>(workspace, L.partial);
+  }
   if (launch_grouped_gemm(d->dtype, d->deterministic ? EPI_DOWN_SLOT : EPI_DOWN_ATOMIC, L.g2.var, h, s) !=
-          hipSuccess ||
-      !mk.mark(4))
+      hipSuccess)
     return MOE_EDEVICE;
+  if (ncu > 0 && launch_split_fixup(h, ncu, s) != hipSuccess) return MOE_EDEVICE;
+  if (!mk.mark(4)) return MOE_EDEVICE;
 
   if (d->deterministic || d->out_dtype == MOE_BF16) {
     FinalizeArgs f{};

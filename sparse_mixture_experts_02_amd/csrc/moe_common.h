@@ -102,8 +102,18 @@ struct WorkSpec {
   int32_t max_work;  // upper bound of the item count (grid size)
   int2* work;        // (max_work) {expert | column_tile << 8, first sorted row}
   int32_t* num_work; // (1)
+  // Split of the last partial round along K (0: off).  With `split_ncu`
+  // compute units and `tiles` items, the R = tiles % split_ncu items past the
+  // last full round are each cut into P = min(4, split_ncu / R) K ranges (when
+  // P >= 2), so they fill one round of shorter blocks.  Such an item in `work`
+  // is {kSplitItem | q, 0} with q = j*P + p: part p of split tile j, whose
+  // {expert | column_tile << 8, first row} is split_tiles[j].
+  int32_t split_ncu;
+  int2* split_tiles;   // (split_ncu)
+  int32_t* split_info; // (2): R, P
 };
 constexpr int kColGroup = 4;  // column tiles per ordering group
+constexpr int32_t kSplitItem = (int32_t)0x80000000;
 
 struct DispatchArgs {
   const int32_t* sel32;   // (M) expert of assignment i = t*K + k; E = dropped
@@ -159,8 +169,19 @@ struct GemmArgs {
   const int32_t* sorted_slot;
   const float* sorted_w;
   int32_t vec_ok;           // rows 16-byte aligned: vector loads allowed
+  // K-split items (down projection, slot epilogue, 256-row tiles only): the
+  // partial sums of part p of split tile j go to partial + (j*P + p) tiles of
+  // BM x 256 fp32, reduced by launch_split_fixup.
+  const int2* split_tiles;
+  const int32_t* split_info;
+  float* partial;
 };
 hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s);
+// Sums the K parts of every split tile in part order and applies the slot
+// epilogue (w * (sum + b2) into the (t,k) slot row).  One block per tile slot;
+// `ncu` blocks, those past R exit.
+constexpr int kSplitTileRows = 256, kSplitTileCols = 256;
+hipError_t launch_split_fixup(const GemmArgs& a, int32_t ncu, hipStream_t s);
 hipError_t launch_gemm_bf16(int epi, int var, const GemmArgs& a, hipStream_t s);
 
 struct FinalizeArgs {
