@@ -99,7 +99,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   // K steps of KB/2 elements; a split item covers steps [kb0, ke0) of its
   // tile and leaves its fp32 partial sums for launch_split_fixup.
   const int nk = (int)(a.Kd / (KB / 2));
-  constexpr bool SPLITTABLE = EPI == EPI_DOWN_SLOT && S == 2 && NW == 8 && NT == 4;
+  constexpr bool SPLITTABLE = EPI == EPI_DOWN_SLOT && (BM == 256 || BM == 32);
   int2 wk = a.work[blockIdx.x];
   int kb0 = 0, ke0 = nk, split_slot = -1;
   if constexpr (SPLITTABLE) {
@@ -153,12 +153,14 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   const char* Abase = static_cast<const char*>(a.A);
   const char* Bbase = static_cast<const char*>(a.B) + (int64_t)e * a.b_estride * 2;
 
-  // Loads of stage kt into its buffer; past the end of K the last stage is
-  // reloaded (into a buffer nobody reads any more), so every step issues the
-  // same number of loads and the wait count is one constant.
+  // Loads of stage kt into its buffer; past the end of the K range the last
+  // stage is reloaded (into a buffer nobody reads any more), so every step
+  // issues the same number of loads and the wait count is one constant.
+  // kb0 <= nk - 1 always, so `klast` is a valid step even for an empty range.
+  const int klast = ke0 - 1 > kb0 ? ke0 - 1 : kb0;
   auto issue = [&](int kt) {
     char* dst = lds + (kt % S) * STAGE;
-    const uint32_t kb = (uint32_t)min(kt, nk - 1) * (uint32_t)KB;
+    const uint32_t kb = (uint32_t)min(kt, klast) * (uint32_t)KB;
 #pragma unroll
     for (int i = 0; i < AI; ++i)
       lds_dma16(Abase + (aoff[i] + kb), dst + (w * AI + i) * 1024);
@@ -319,8 +321,8 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     };
 
 #pragma unroll
-    for (int p = 0; p < S - 1; ++p) issue(p);
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int p = 0; p < S - 1; ++p) issue(kb0 + p);
+    for (int kt = kb0; kt < ke0; ++kt) {
       wait_vm<(S - 2) * NI>();
       barrier_lds();
       issue(kt + S - 1);
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmArgs a) {
   const int2 wk = a.split_tiles[j];
   const int e = wk.x & 0xff;
   const int r0 = wk.y;
-  const int rows = min(kSplitTileRows, a.offsets[e + 1] - r0);
+  const int rows = min(a.split_bm, a.offsets[e + 1] - r0);
   const int64_t n0 = (int64_t)(wk.x >> 8) * kSplitTileCols;
   const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;
   constexpr int C4 = kSplitTileCols / 4;

@@ -90,10 +90,11 @@ Layout layout_of(const moe_desc* d) {
   L.nchunks = (int32_t)((M + kDispatchChunk - 1) / kDispatchChunk);
   L.g1 = plan_gemm(d, M, F, D, T, G * F * D, swiglu);
   L.g2 = plan_gemm(d, M, D, F, M, D * F, false);
-  // Deterministic mode with 256-row tiles: the down projection's items past
-  // its last full round of CUs are cut along K (fp32 partial tiles, reduced in
-  // part order by a fix-up kernel) so they fill one round of shorter blocks.
-  L.split2 = d->deterministic && L.g2.var == VAR_BF16_M256;
+  // Deterministic mode with 256- or 32-row tiles: the down projection's items
+  // past its last full round of CUs are cut along K (fp32 partial tiles,
+  // reduced in part order by a fix-up kernel) so they fill one round of
+  // shorter blocks (decode: 8 experts x 16 column tiles is half a round).
+  L.split2 = d->deterministic && (L.g2.var == VAR_BF16_M256 || L.g2.var == VAR_BF16_M32);
   if (L.split2) L.g2.max_work += kSplitMaxCU;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -371,6 +372,7 @@ moe_status forward_impl(const moe_desc* d, const moe_routing* r, const void* x, 
     h.split_tiles = at<int2>(workspace, L.split_tiles);
     h.split_info = at<int32_t>(workspace, L.split_info);
     h.partial = at<float>(workspace, L.partial);
+    h.split_bm = L.g2.bm;
   }
   if (launch_grouped_gemm(d->dtype, d->deterministic ? EPI_DOWN_SLOT : EPI_DOWN_ATOMIC, L.g2.var, h, s) !=
       hipSuccess)

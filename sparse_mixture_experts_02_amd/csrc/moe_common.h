@@ -169,12 +169,13 @@ struct GemmArgs {
   const int32_t* sorted_slot;
   const float* sorted_w;
   int32_t vec_ok;           // rows 16-byte aligned: vector loads allowed
-  // K-split items (down projection, slot epilogue, 256-row tiles only): the
+  // K-split items (down projection, slot epilogue, 256- and 32-row tiles): the
   // partial sums of part p of split tile j go to partial + (j*P + p) tiles of
   // BM x 256 fp32, reduced by launch_split_fixup.
   const int2* split_tiles;
   const int32_t* split_info;
   float* partial;
+  int32_t split_bm;         // rows per split tile (the kernel variant's tile height)
 };
 hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s);
 // Sums the K parts of every split tile in part order and applies the slot
