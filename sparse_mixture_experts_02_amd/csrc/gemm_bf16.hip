@@ -99,7 +99,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   // K steps of KB/2 elements; a split item covers steps [kb0, ke0) of its
   // tile and leaves its fp32 partial sums for launch_split_fixup.
   const int nk = (int)(a.Kd / (KB / 2));
-  constexpr bool SPLITTABLE = EPI == EPI_DOWN_SLOT && (BM == 256 || BM == 32);
+  constexpr bool SPLITTABLE = EPI != EPI_DOWN_ATOMIC && (BM == 256 || BM == 32);
   int2 wk = a.work[blockIdx.x];
   int kb0 = 0, ke0 = nk, split_slot = -1;
   if constexpr (SPLITTABLE) {
@@ -334,20 +334,23 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   if constexpr (SPLITTABLE) {
     if (split_slot >= 0) {
       // raw fp32 partial sums of this K range, tile-local rows x 256 columns
+      // (SwiGLU: the gate sums in columns [0,128), the up sums in [128,256))
       float* dst = a.partial + (int64_t)split_slot * (kSplitTileRows * kSplitTileCols);
 #pragma unroll
       for (int mi = 0; mi < SM; ++mi) {
         const int m = wm * WM + mi * 32 + l32;
         if (m >= rows) continue;
 #pragma unroll
-        for (int ni = 0; ni < SN; ++ni)
+        for (int q = 0; q < NACC; ++q)
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x16& c0 = acc[0][mi][ni];
-            const int c = wn * WN + ni * 32 + 8 * q4 + 4 * h;
-            *reinterpret_cast<float4*>(dst + m * kSplitTileCols + c) =
-                float4{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
-          }
+          for (int ni = 0; ni < SN; ++ni)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const f32x16& c0 = acc[q][mi][ni];
+              const int c = q * OUTC + wn * WN + ni * 32 + 8 * q4 + 4 * h;
+              *reinterpret_cast<float4*>(dst + m * kSplitTileCols + c) =
+                  float4{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
+            }
       }
       return;
     }
@@ -373,32 +376,43 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 }
 
 // Reduction of the split tiles: block j sums the P partial tiles of split
-// tile j in part order (reproducible) and applies the slot epilogue, the same
-// w * (acc + b2) store as an unsplit tile.
+// tile j in part order (reproducible) and applies the tile's epilogue to the
+// sums, exactly as an unsplit tile applies it to its accumulators (SwiGLU:
+// gate and up sums; ReLU; the down projection's weighted slot store).
+template <int EPI>
 __global__ __launch_bounds__(256) void split_fixup_kernel(GemmArgs a) {
   const int R = a.split_info[0], P = a.split_info[1];
   const int j = blockIdx.x;
   if (j >= R) return;
+  constexpr bool DUAL = EPI == EPI_SWIGLU;
+  constexpr int OUTC = DUAL ? kSplitTileCols / 2 : kSplitTileCols;
   const int2 wk = a.split_tiles[j];
   const int e = wk.x & 0xff;
   const int r0 = wk.y;
   const int rows = min(a.split_bm, a.offsets[e + 1] - r0);
-  const int64_t n0 = (int64_t)(wk.x >> 8) * kSplitTileCols;
+  const int64_t n0 = (int64_t)(wk.x >> 8) * OUTC;
   const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;
-  constexpr int C4 = kSplitTileCols / 4;
+  constexpr int C4 = OUTC / 4;
   for (int idx = threadIdx.x; idx < rows * C4; idx += 256) {
     const int m = idx / C4, c = (idx - m * C4) * 4;
-    f32x4 sum{0.f, 0.f, 0.f, 0.f};
+    f32x4 s0{0.f, 0.f, 0.f, 0.f}, s1{0.f, 0.f, 0.f, 0.f};
     for (int p = 0; p < P; ++p) {
-      const float4 v = *reinterpret_cast<const float4*>(
-          a.partial + ((int64_t)(j * P + p) * kSplitTileRows + m) * kSplitTileCols + c);
-      sum[0] += v.x;
-      sum[1] += v.y;
-      sum[2] += v.z;
-      sum[3] += v.w;
+      const float* src = a.partial + ((int64_t)(j * P + p) * kSplitTileRows + m) * kSplitTileCols + c;
+      const float4 v = *reinterpret_cast<const float4*>(src);
+      s0[0] += v.x;
+      s0[1] += v.y;
+      s0[2] += v.z;
+      s0[3] += v.w;
+      if constexpr (DUAL) {
+        const float4 u = *reinterpret_cast<const float4*>(src + OUTC);
+        s1[0] += u.x;
+        s1[1] += u.y;
+        s1[2] += u.z;
+        s1[3] += u.w;
+      }
     }
-    const RowCtx rc = row_ctx<EPI_DOWN_SLOT>(a, r0 + m);
-    epilogue4<float, EPI_DOWN_SLOT>(a, rc, n0 + c, sum, sum, bias);
+    const RowCtx rc = row_ctx<EPI>(a, r0 + m);
+    epilogue4<uint16_t, EPI>(a, rc, n0 + c, s0, s1, bias);
   }
 }
 
@@ -420,9 +434,21 @@ hipError_t launch_rows(int var, const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_split_fixup(const GemmArgs& a, int32_t ncu, hipStream_t s) {
+hipError_t launch_split_fixup(int epi, const GemmArgs& a, int32_t ncu, hipStream_t s) {
   if (ncu <= 0) return hipSuccess;
-  hipLaunchKernelGGL(split_fixup_kernel, dim3(ncu), dim3(256), 0, s, a);
+  switch (epi) {
+    case EPI_SWIGLU:
+      hipLaunchKernelGGL(split_fixup_kernel<EPI_SWIGLU>, dim3(ncu), dim3(256), 0, s, a);
+      break;
+    case EPI_RELU:
+      hipLaunchKernelGGL(split_fixup_kernel<EPI_RELU>, dim3(ncu), dim3(256), 0, s, a);
+      break;
+    case EPI_DOWN_SLOT:
+      hipLaunchKernelGGL(split_fixup_kernel<EPI_DOWN_SLOT>, dim3(ncu), dim3(256), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

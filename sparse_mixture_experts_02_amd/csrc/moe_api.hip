@@ -24,17 +24,16 @@ struct GemmPlan {
   int32_t bm = 128, cols = 128, ntn = 0, max_work = 0;
 };
 
-// Compute units the K-split of the down projection's last round is planned
-// for (the split buffers are sized for this many; a part with more CUs plans
-// for this many).
+// Compute units the K-split of a GEMM's last round is planned for (the split
+// buffers are sized for this many; a part with more CUs plans for this many).
 constexpr int32_t kSplitMaxCU = 256;
 
 struct Layout {
   int64_t M = 0;
   int32_t nchunks = 0;
   GemmPlan g1, g2;
-  bool split2 = false;  // the down projection may cut its last round along K
-  size_t split_tiles = 0, split_info = 0, partial = 0;
+  bool split1 = false, split2 = false;  // gate_up / down may cut their last round along K
+  size_t split_tiles1 = 0, split_info1 = 0, split_tiles2 = 0, split_info2 = 0, partial = 0;
   size_t sel32 = 0, chunk_counts = 0, chunk_base = 0, counts = 0, offsets = 0, work1 = 0, work2 = 0,
          num_work = 0, sorted_tok = 0, sorted_slot = 0, sorted_w = 0, logits = 0, stats_part = 0, h = 0, slots = 0,
          acc = 0, total = 0;
@@ -90,11 +89,16 @@ Layout layout_of(const moe_desc* d) {
   L.nchunks = (int32_t)((M + kDispatchChunk - 1) / kDispatchChunk);
   L.g1 = plan_gemm(d, M, F, D, T, G * F * D, swiglu);
   L.g2 = plan_gemm(d, M, D, F, M, D * F, false);
-  // Deterministic mode with 256- or 32-row tiles: the down projection's items
-  // past its last full round of CUs are cut along K (fp32 partial tiles,
-  // reduced in part order by a fix-up kernel) so they fill one round of
-  // shorter blocks (decode: 8 experts x 16 column tiles is half a round).
-  L.split2 = d->deterministic && (L.g2.var == VAR_BF16_M256 || L.g2.var == VAR_BF16_M32);
+  // With 256- or 32-row tiles, a GEMM's items past its last full round of CUs
+  // are cut along K (fp32 partial tiles, reduced in part order by a fix-up
+  // kernel that then applies the epilogue) so they fill one round of shorter
+  // blocks (decode: 8 experts x 16 down column tiles is half a round).  The
+  // down projection splits only in deterministic mode (the atomic combine
+  // would add more than two terms per output).
+  auto splits = [](int var) { return var == VAR_BF16_M256 || var == VAR_BF16_M32; };
+  L.split1 = splits(L.g1.var);
+  L.split2 = d->deterministic && splits(L.g2.var);
+  if (L.split1) L.g1.max_work += kSplitMaxCU;
   if (L.split2) L.g2.max_work += kSplitMaxCU;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -117,11 +121,16 @@ Layout layout_of(const moe_desc* d) {
   L.stats_part = take(sizeof(float) * (size_t)router_blocks(T) * 3 * E);
   L.h = take((size_t)elem_bytes(d->dtype) * M * F);
   if (d->deterministic) L.slots = take(sizeof(float) * M * D);
-  if (L.split2) {
-    L.split_tiles = take(sizeof(int2) * kSplitMaxCU);
-    L.split_info = take(sizeof(int32_t) * 2);
-    L.partial = take(sizeof(float) * (size_t)kSplitMaxCU * kSplitTileRows * kSplitTileCols);
+  if (L.split1) {
+    L.split_tiles1 = take(sizeof(int2) * kSplitMaxCU);
+    L.split_info1 = take(sizeof(int32_t) * 2);
   }
+  if (L.split2) {
+    L.split_tiles2 = take(sizeof(int2) * kSplitMaxCU);
+    L.split_info2 = take(sizeof(int32_t) * 2);
+  }
+  if (L.split1 || L.split2)  // shared: the two GEMMs and their fix-ups run in order
+    L.partial = take(sizeof(float) * (size_t)kSplitMaxCU * kSplitTileRows * kSplitTileCols);
   if (!d->deterministic && d->out_dtype == MOE_BF16) L.acc = take(sizeof(float) * T * D);
   L.total = off;
   return L;
@@ -263,10 +272,18 @@ moe_status route_and_sort(const moe_desc* d, const RoutePlan& rp, const Layout& 
     da.spec[i].work = at<int2>(ws, works[i]);
     da.spec[i].num_work = at<int32_t>(ws, L.num_work) + i;
   }
-  if (L.split2 && build_work) {
-    da.spec[1].split_ncu = device_cus();
-    da.spec[1].split_tiles = at<int2>(ws, L.split_tiles);
-    da.spec[1].split_info = at<int32_t>(ws, L.split_info);
+  if (build_work && (L.split1 || L.split2)) {
+    const int32_t ncu = device_cus();
+    if (L.split1) {
+      da.spec[0].split_ncu = ncu;
+      da.spec[0].split_tiles = at<int2>(ws, L.split_tiles1);
+      da.spec[0].split_info = at<int32_t>(ws, L.split_info1);
+    }
+    if (L.split2) {
+      da.spec[1].split_ncu = ncu;
+      da.spec[1].split_tiles = at<int2>(ws, L.split_tiles2);
+      da.spec[1].split_info = at<int32_t>(ws, L.split_info2);
+    }
   }
   if (rp.capacity) {
     // Sort the (threshold-kept) assignments once, drop the slots past each
@@ -344,9 +361,17 @@ moe_status forward_impl(const moe_desc* d, const moe_routing* r, const void* x, 
   g.sorted_slot = at<int32_t>(workspace, L.sorted_slot);
   g.sorted_w = at<float>(workspace, L.sorted_w);
   g.vec_ok = aligned16(x) && aligned16(gate_up_proj) && ((d->D * eb) % 16 == 0);
-  if (launch_grouped_gemm(d->dtype, swiglu ? EPI_SWIGLU : EPI_RELU, L.g1.var, g, s) != hipSuccess ||
-      !mk.mark(3))
-    return MOE_EDEVICE;
+  const int32_t ncu = (L.split1 || L.split2) ? device_cus() : 0;
+  if (L.split1) {
+    g.split_tiles = at<int2>(workspace, L.split_tiles1);
+    g.split_info = at<int32_t>(workspace, L.split_info1);
+    g.partial = at<float>(workspace, L.partial);
+    g.split_bm = L.g1.bm;
+  }
+  const int epi1 = swiglu ? EPI_SWIGLU : EPI_RELU;
+  if (launch_grouped_gemm(d->dtype, epi1, L.g1.var, g, s) != hipSuccess) return MOE_EDEVICE;
+  if (L.split1 && ncu > 0 && launch_split_fixup(epi1, g, ncu, s) != hipSuccess) return MOE_EDEVICE;
+  if (!mk.mark(3)) return MOE_EDEVICE;
 
   GemmArgs h = g;
   h.A = at<void>(workspace, L.h);
@@ -366,18 +391,19 @@ moe_status forward_impl(const moe_desc* d, const moe_routing* r, const void* x, 
   h.num_work = at<int32_t>(workspace, L.num_work) + 1;
   h.max_work = L.g2.max_work;
   h.vec_ok = aligned16(down_proj) && ((d->F * eb) % 16 == 0);
-  int32_t ncu = 0;
+  h.split_tiles = nullptr;
+  h.split_info = nullptr;
+  h.partial = nullptr;
   if (L.split2) {
-    ncu = device_cus();
-    h.split_tiles = at<int2>(workspace, L.split_tiles);
-    h.split_info = at<int32_t>(workspace, L.split_info);
+    h.split_tiles = at<int2>(workspace, L.split_tiles2);
+    h.split_info = at<int32_t>(workspace, L.split_info2);
     h.partial = at<float>(workspace, L.partial);
     h.split_bm = L.g2.bm;
   }
   if (launch_grouped_gemm(d->dtype, d->deterministic ? EPI_DOWN_SLOT : EPI_DOWN_ATOMIC, L.g2.var, h, s) !=
       hipSuccess)
     return MOE_EDEVICE;
-  if (ncu > 0 && launch_split_fixup(h, ncu, s) != hipSuccess) return MOE_EDEVICE;
+  if (L.split2 && ncu > 0 && launch_split_fixup(EPI_DOWN_SLOT, h, ncu, s) != hipSuccess) return MOE_EDEVICE;
   if (!mk.mark(4)) return MOE_EDEVICE;
 
   if (d->deterministic || d->out_dtype == MOE_BF16) {

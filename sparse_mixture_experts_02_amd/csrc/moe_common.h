@@ -169,20 +169,20 @@ struct GemmArgs {
   const int32_t* sorted_slot;
   const float* sorted_w;
   int32_t vec_ok;           // rows 16-byte aligned: vector loads allowed
-  // K-split items (down projection, slot epilogue, 256- and 32-row tiles): the
-  // partial sums of part p of split tile j go to partial + (j*P + p) tiles of
-  // BM x 256 fp32, reduced by launch_split_fixup.
+  // K-split items (256- and 32-row bf16 tiles, any epilogue but the atomic
+  // combine): the partial sums of part p of split tile j go to partial +
+  // (j*P + p) tiles of 256 x 256 fp32, reduced by launch_split_fixup.
   const int2* split_tiles;
   const int32_t* split_info;
   float* partial;
   int32_t split_bm;         // rows per split tile (the kernel variant's tile height)
 };
 hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s);
-// Sums the K parts of every split tile in part order and applies the slot
-// epilogue (w * (sum + b2) into the (t,k) slot row).  One block per tile slot;
-// `ncu` blocks, those past R exit.
+// Sums the K parts of every split tile in part order and applies the tile's
+// epilogue `epi` (SwiGLU, ReLU or the down projection's slot store) to the
+// sums.  One block per tile slot; `ncu` blocks, those past R exit.
 constexpr int kSplitTileRows = 256, kSplitTileCols = 256;
-hipError_t launch_split_fixup(const GemmArgs& a, int32_t ncu, hipStream_t s);
+hipError_t launch_split_fixup(int epi, const GemmArgs& a, int32_t ncu, hipStream_t s);
 hipError_t launch_gemm_bf16(int epi, int var, const GemmArgs& a, hipStream_t s);
 
 struct FinalizeArgs {
