@@ -375,14 +375,18 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
-// Reduction of the split tiles: block j sums the P partial tiles of split
-// tile j in part order (reproducible) and applies the tile's epilogue to the
+// Reduction of the split tiles: kFixupBlocksPerTile blocks share the rows of
+// split tile j; each sums the P partial tiles in part order (reproducible)
+// and applies the tile's epilogue to the
 // sums, exactly as an unsplit tile applies it to its accumulators (SwiGLU:
 // gate and up sums; ReLU; the down projection's weighted slot store).
+constexpr int kFixupBlocksPerTile = 4;
+
 template <int EPI>
 __global__ __launch_bounds__(256) void split_fixup_kernel(GemmArgs a) {
   const int R = a.split_info[0], P = a.split_info[1];
-  const int j = blockIdx.x;
+  const int j = blockIdx.x / kFixupBlocksPerTile;
+  const int sub = blockIdx.x - j * kFixupBlocksPerTile;
   if (j >= R) return;
   constexpr bool DUAL = EPI == EPI_SWIGLU;
   constexpr int OUTC = DUAL ? kSplitTileCols / 2 : kSplitTileCols;
@@ -390,10 +394,13 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmArgs a) {
   const int e = wk.x & 0xff;
   const int r0 = wk.y;
   const int rows = min(a.split_bm, a.offsets[e + 1] - r0);
+  // this block's share of the tile's rows
+  const int rs = (a.split_bm + kFixupBlocksPerTile - 1) / kFixupBlocksPerTile;
+  const int m0 = sub * rs, m1 = min(rows, m0 + rs);
   const int64_t n0 = (int64_t)(wk.x >> 8) * OUTC;
   const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;
   constexpr int C4 = OUTC / 4;
-  for (int idx = threadIdx.x; idx < rows * C4; idx += 256) {
+  for (int idx = m0 * C4 + (int)threadIdx.x; idx < m1 * C4; idx += 256) {
     const int m = idx / C4, c = (idx - m * C4) * 4;
     f32x4 s0{0.f, 0.f, 0.f, 0.f}, s1{0.f, 0.f, 0.f, 0.f};
     for (int p = 0; p < P; ++p) {
@@ -438,13 +445,13 @@ hipError_t launch_split_fixup(int epi, const GemmArgs& a, int32_t ncu, hipStream
   if (ncu <= 0) return hipSuccess;
   switch (epi) {
     case EPI_SWIGLU:
-      hipLaunchKernelGGL(split_fixup_kernel<EPI_SWIGLU>, dim3(ncu), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(split_fixup_kernel<EPI_SWIGLU>, dim3(ncu * kFixupBlocksPerTile), dim3(256), 0, s, a);
       break;
     case EPI_RELU:
-      hipLaunchKernelGGL(split_fixup_kernel<EPI_RELU>, dim3(ncu), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(split_fixup_kernel<EPI_RELU>, dim3(ncu * kFixupBlocksPerTile), dim3(256), 0, s, a);
       break;
     case EPI_DOWN_SLOT:
-      hipLaunchKernelGGL(split_fixup_kernel<EPI_DOWN_SLOT>, dim3(ncu), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(split_fixup_kernel<EPI_DOWN_SLOT>, dim3(ncu * kFixupBlocksPerTile), dim3(256), 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;

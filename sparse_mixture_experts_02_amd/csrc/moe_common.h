@@ -180,7 +180,7 @@ struct GemmArgs {
 hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s);
 // Sums the K parts of every split tile in part order and applies the tile's
 // epilogue `epi` (SwiGLU, ReLU or the down projection's slot store) to the
-// sums.  One block per tile slot; `ncu` blocks, those past R exit.
+// sums.  Four blocks per tile slot, `ncu` slots; blocks past R's exit.
 constexpr int kSplitTileRows = 256, kSplitTileCols = 256;
 hipError_t launch_split_fixup(int epi, const GemmArgs& a, int32_t ncu, hipStream_t s);
 hipError_t launch_gemm_bf16(int epi, int var, const GemmArgs& a, hipStream_t s);
