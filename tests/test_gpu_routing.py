@@ -331,3 +331,43 @@ def test_prefill_capacity_full_size_sampled():
     st = compare(inp, g, ref, tokens=tok)
     compare_stats(inp, g, ref)
     _say("slots %d dropped %d err %g exempt %d" % (ref["slots"], int((~ref["kept"]).sum()), st, ex))
+
+
+@pytest.mark.slow
+def test_fine_experts_threshold_and_capacity_full_size_sampled():
+    """The 128-expert workload (T=16384, K=8, Zipf-skewed loads) with a
+    dynamic threshold and capacity factor 1.25 over four 4096-token
+    sequences: kept flags, counts and statistics for every token, outputs on
+    sampled tokens."""
+    inp = workloads.generate("fine")
+    T = inp["cfg"]["T"]
+    thr = safe_threshold(inp, 0.3)
+    rng = np.random.default_rng(4)
+    tok = np.unique(np.concatenate([rng.choice(T, 24, replace=False), [0, T - 1]]))
+    _say("fine threshold %.6f + capacity 1.25 x 4096" % thr)
+    g = run_gpu(inp, dynamic_threshold=thr, capacity_factor=1.25, seq_len=4096)
+    ref, ex = reference(inp, g, tokens=tok, threshold=thr, capacity_factor=1.25, seq_len=4096)
+    st = compare(inp, g, ref, tokens=tok)
+    compare_stats(inp, g, ref)
+    _say("slots %d dropped %d err %g exempt %d" % (ref["slots"], int((~ref["kept"]).sum()), st, ex))
+
+
+@pytest.mark.slow
+def test_prefill_replay_full_size_sampled():
+    """The Mixtral-shaped prefill replaying a record that differs from the own
+    selection (each covered token's experts shifted by one) on 60% of the
+    tokens."""
+    inp = workloads.generate("prefill")
+    c = inp["cfg"]
+    T, E, K = c["T"], c["E"], c["K"]
+    own = oracle.route(inp["x"], inp["router"], top_k=K)["sel"]
+    record = (own + 1) % E
+    mask = np.random.default_rng(6).random(T) < 0.6
+    rng = np.random.default_rng(7)
+    tok = np.unique(np.concatenate([rng.choice(T, 40, replace=False), [0, T - 1]]))
+    _say("prefill replay T=%d covered=%d" % (T, mask.sum()))
+    g = run_gpu(inp, replay=record, replay_mask=mask)
+    ref, ex = reference(inp, g, tokens=tok, replay=record, replay_mask=mask)
+    st = compare(inp, g, ref, tokens=tok)
+    np.testing.assert_array_equal(g["sel"][mask], record[mask])
+    _say("err %g exempt %d" % (st, ex))
