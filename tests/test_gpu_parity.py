@@ -262,3 +262,57 @@ def test_fine_grained_128_experts_sampled(name):
         g2 = gpu_forward(inp, dict(d, gate_up=gu, down=dn), deterministic=True)
         assert np.array_equal(g2["out"], g["out"])
     _CACHE.pop(name, None)
+
+
+def test_token_permutation_equivariance():
+    """Permuting the tokens permutes the outputs (the exercise's layer mixes no
+    tokens): same selections and weights bitwise, outputs within the fp32 bar
+    (a permutation moves rows between tiles and K-split parts, which may change
+    the fp32 summation order of the down projection)."""
+    inp = workloads.generate(workloads.small_config(2048, 256, 512, 4, 2, dtype="bf16", cfg_id=950))
+    perm = np.random.default_rng(9).permutation(2048)
+    a = gpu_forward(inp)
+    pinp = dict(inp, x=inp["x"][perm])
+    b = gpu_forward(pinp)
+    np.testing.assert_array_equal(b["sel"], a["sel"][perm])
+    np.testing.assert_array_equal(b["weights"], a["weights"][perm])
+    np.testing.assert_array_equal(b["logits"], a["logits"][perm])
+    ref = a["out"][perm].astype(np.float64)
+    err = np.abs(b["out"] - ref)
+    assert err.max() <= 1e-5 * max(np.abs(ref).max(), 1e-30), err.max()
+
+
+def test_timed_entry_point_matches_forward():
+    """moe_forward_timed is moe_forward plus event records: bitwise equal outputs."""
+    import ctypes
+    inp = workloads.generate(workloads.small_config(1000, 128, 256, 8, 2, dtype="bf16", cfg_id=951))
+    d = device_inputs(inp)
+    c = inp["cfg"]
+    T, D, F, E, K = c["T"], c["D"], c["F"], c["E"], c["K"]
+    desc = moe.make_desc(T, D, F, E, K, dtype=torch.bfloat16, deterministic=True)
+    nbytes = moe.moe_workspace_bytes(desc)
+    outs = []
+    for timed in (False, True):
+        ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
+        out = torch.empty((T, D), dtype=torch.float32, device="cuda")
+        sel = torch.empty((T, K), dtype=torch.int64, device="cuda")
+        w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        args = [d["x"].data_ptr(), d["router"].data_ptr(), d["gate_up"].data_ptr(), d["down"].data_ptr(), None, None,
+                None, out.data_ptr(), sel.data_ptr(), w.data_ptr(), None, None, ws.data_ptr(), nbytes, stream]
+        if timed:
+            import bench
+            hip = bench.Hip()
+            evs = [hip.event() for _ in range(moe.MOE_STAGE_EVENTS)]
+            handles = (ctypes.c_void_p * moe.MOE_STAGE_EVENTS)(*evs)
+            assert moe.moe_forward_timed(desc, *args, handles, moe.MOE_STAGE_EVENTS) == moe.MOE_OK
+            torch.cuda.synchronize()
+            assert hip.elapsed_ms(evs[0], evs[-1]) > 0.0
+            for ev in evs:
+                hip.destroy(ev)
+        else:
+            assert moe.moe_forward(desc, *args) == moe.MOE_OK
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy(), sel.cpu().numpy(), w.cpu().numpy()))
+    for x, y in zip(*outs):
+        np.testing.assert_array_equal(x, y)
