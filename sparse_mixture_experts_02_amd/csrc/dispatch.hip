@@ -70,57 +70,15 @@ __device__ __forceinline__ int xcd_order(int b, int total) {
   return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(DispatchArgs a) {
-  __shared__ int part[kScanThreads];   // [J][E] partial chunk sums, then their prefixes
-  __shared__ int tmp[kScanThreads];
-  __shared__ int offs[kMaxExperts + 1];
-  __shared__ int tst[kMaxExperts + 1];
-  __shared__ int cnts[kMaxExperts];
+// Work lists of the grouped GEMMs from the per-expert counts `cnts` and
+// segment offsets `offs` (both in LDS).  Order: experts ascending; inside an
+// expert, groups of kColGroup column tiles; inside a group, column tile
+// slowest and row tile fastest.  Empty experts contribute no item.  Called by
+// all kScanThreads threads of one block; `tst` (E+1) and `tmp`
+// (kScanThreads) are LDS scratch.
+__device__ void build_work_lists(const DispatchArgs& a, const int* cnts, const int* offs, int* tst, int* tmp) {
   const int tid = threadIdx.x;
   const int E = a.E;
-  const int J = kScanThreads / E;      // chunk-range lanes per expert
-  const int e = tid % E, j = tid / E;
-  const bool worker = j < J;
-  const int nch = a.nchunks;
-  const int cb = worker ? (int)((int64_t)j * nch / J) : 0;
-  const int ce = worker ? (int)((int64_t)(j + 1) * nch / J) : 0;
-
-  int s = 0;
-  for (int b = cb; b < ce; ++b) s += a.chunk_counts[(int64_t)b * E + e];
-  if (worker) part[j * E + e] = s;
-  __syncthreads();
-  if (tid < E) {
-    int run = 0;
-    for (int jj = 0; jj < J; ++jj) {
-      const int v = part[jj * E + tid];
-      part[jj * E + tid] = run;
-      run += v;
-    }
-    offs[tid] = run;  // count, scanned below
-    cnts[tid] = run;
-    a.counts[tid] = run;
-    if (a.counts_out) a.counts_out[tid] = run;
-  }
-  __syncthreads();
-  const int M = block_exclusive_scan(offs, tmp, E);
-  if (tid == 0) offs[E] = M;
-  if (tid <= E) {
-    a.offsets[tid] = offs[tid];
-    if (a.offsets_out) a.offsets_out[tid] = offs[tid];
-  }
-  if (worker) {
-    int base = offs[e] + part[j * E + e];
-    for (int b = cb; b < ce; ++b) {
-      const int64_t idx = (int64_t)b * E + e;
-      const int c = a.chunk_counts[idx];
-      a.chunk_base[idx] = base;
-      base += c;
-    }
-  }
-
-  // Work lists of the grouped GEMMs.  Order: experts ascending; inside an
-  // expert, groups of kColGroup column tiles; inside a group, column tile
-  // slowest and row tile fastest.  Empty experts contribute no item.
   for (int g = 0; g < a.nspec; ++g) {
     const WorkSpec& sp = a.spec[g];
     __syncthreads();
@@ -181,6 +139,57 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DispatchArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(DispatchArgs a) {
+  __shared__ int part[kScanThreads];   // [J][E] partial chunk sums, then their prefixes
+  __shared__ int tmp[kScanThreads];
+  __shared__ int offs[kMaxExperts + 1];
+  __shared__ int tst[kMaxExperts + 1];
+  __shared__ int cnts[kMaxExperts];
+  const int tid = threadIdx.x;
+  const int E = a.E;
+  const int J = kScanThreads / E;      // chunk-range lanes per expert
+  const int e = tid % E, j = tid / E;
+  const bool worker = j < J;
+  const int nch = a.nchunks;
+  const int cb = worker ? (int)((int64_t)j * nch / J) : 0;
+  const int ce = worker ? (int)((int64_t)(j + 1) * nch / J) : 0;
+
+  int s = 0;
+  for (int b = cb; b < ce; ++b) s += a.chunk_counts[(int64_t)b * E + e];
+  if (worker) part[j * E + e] = s;
+  __syncthreads();
+  if (tid < E) {
+    int run = 0;
+    for (int jj = 0; jj < J; ++jj) {
+      const int v = part[jj * E + tid];
+      part[jj * E + tid] = run;
+      run += v;
+    }
+    offs[tid] = run;  // count, scanned below
+    cnts[tid] = run;
+    a.counts[tid] = run;
+    if (a.counts_out) a.counts_out[tid] = run;
+  }
+  __syncthreads();
+  const int M = block_exclusive_scan(offs, tmp, E);
+  if (tid == 0) offs[E] = M;
+  if (tid <= E) {
+    a.offsets[tid] = offs[tid];
+    if (a.offsets_out) a.offsets_out[tid] = offs[tid];
+  }
+  if (worker) {
+    int base = offs[e] + part[j * E + e];
+    for (int b = cb; b < ce; ++b) {
+      const int64_t idx = (int64_t)b * E + e;
+      const int c = a.chunk_counts[idx];
+      a.chunk_base[idx] = base;
+      base += c;
+    }
+  }
+
+  build_work_lists(a, cnts, offs, tst, tmp);
+}
+
 __global__ __launch_bounds__(kThreads) void scatter_kernel(DispatchArgs a) {
   __shared__ int running[kMaxExperts];
   __shared__ int wcount[kThreads / 64][kMaxExperts];
@@ -231,6 +240,67 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(DispatchArgs a) {
   }
 }
 
+// The whole sort for T*K <= kScanThreads assignments (decode-sized calls) in
+// one block of kScanThreads threads: thread i owns assignment i.  Counts,
+// offsets and work lists as in scan_kernel; the stable rank of assignment i
+// inside its expert is its rank among equal experts of its wave (nine
+// ballots) plus the counts of the earlier waves, so the order inside a
+// segment is increasing (t, k) as in scatter_kernel.
+__global__ __launch_bounds__(kScanThreads) void dispatch_small_kernel(DispatchArgs a) {
+  constexpr int W = kScanThreads / 64;
+  __shared__ int tmp[kScanThreads];
+  __shared__ int offs[kMaxExperts + 1];
+  __shared__ int tst[kMaxExperts + 1];
+  __shared__ int cnts[kMaxExperts];
+  __shared__ int wcount[W][kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int E = a.E;
+  for (int x = tid; x < E; x += kScanThreads) {
+    cnts[x] = 0;
+#pragma unroll
+    for (int q = 0; q < W; ++q) wcount[q][x] = 0;
+  }
+  __syncthreads();
+  const int ei = tid < a.M ? a.sel32[tid] : E;
+  const bool valid = ei < E;                 // E: past the end, or a dropped assignment
+  const int e = valid ? ei : kMaxExperts;    // the sentinel only matches itself
+  uint64_t same = ~0ull;
+#pragma unroll
+  for (int bit = 0; bit < 9; ++bit) {
+    const int on = (e >> bit) & 1;
+    const uint64_t b = __ballot(on);
+    same &= on ? b : ~b;
+  }
+  const int rank = __popcll(same & ((1ull << lane) - 1ull));
+  if (valid && rank == 0) wcount[w][e] = __popcll(same);
+  __syncthreads();
+  if (tid < E) {
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < W; ++q) c += wcount[q][tid];
+    cnts[tid] = c;
+    offs[tid] = c;
+    a.counts[tid] = c;
+    if (a.counts_out) a.counts_out[tid] = c;
+  }
+  __syncthreads();
+  const int M = block_exclusive_scan(offs, tmp, E);
+  if (tid == 0) offs[E] = M;
+  if (tid <= E) {
+    a.offsets[tid] = offs[tid];
+    if (a.offsets_out) a.offsets_out[tid] = offs[tid];
+  }
+  __syncthreads();
+  if (valid) {
+    int pos = offs[e] + rank;
+    for (int q = 0; q < w; ++q) pos += wcount[q][e];
+    a.sorted_tok[pos] = (int32_t)(tid / a.K);
+    a.sorted_slot[pos] = (int32_t)tid;
+    if (a.sorted_w) a.sorted_w[pos] = a.weights[tid];
+  }
+  build_work_lists(a, cnts, offs, tst, tmp);
+}
+
 // Capacity (the Dew "Mixture of experts" page, section "Expert computation
 // and placement", capacity_factor): each sequence keeps at most `slots`
 // assignments per expert, the first in token order.  In the stable sorted
@@ -275,6 +345,10 @@ hipError_t launch_capacity(const CapacityArgs& a, hipStream_t s) {
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
+  if (a.M <= kScanThreads) {
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(count_kernel, dim3(a.nchunks), dim3(kThreads), 0, s, a);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
   hipLaunchKernelGGL(scatter_kernel, dim3(a.nchunks), dim3(kThreads), 0, s, a);

@@ -166,8 +166,9 @@ def test_deterministic_runs_are_bitwise_identical():
     assert np.array_equal(a2["out"], b2["out"])
 
 
-def test_dispatch_is_a_stable_counting_sort():
-    cfg = workloads.small_config(3000, 64, 64, 24, 3, dtype="bf16", router_bias="zipf", cfg_id=404)
+@pytest.mark.parametrize("T", [3000, 341, 1])  # multi-block sort; one-block sort (T*K <= 1024); one token
+def test_dispatch_is_a_stable_counting_sort(T):
+    cfg = workloads.small_config(T, 64, 64, 24, 3, dtype="bf16", router_bias="zipf", cfg_id=404)
     inp = workloads.generate(cfg)
     d = device_inputs(inp)
     r = moe.dispatch(d["x"], d["router"], top_k=3, router_bias=d["router_bias"])
