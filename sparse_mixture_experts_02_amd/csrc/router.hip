@@ -71,7 +71,7 @@ __device__ __forceinline__ void logits_partial(const RouterArgs& a, int64_t t0, 
 
   // U k-steps per iteration: all their loads are issued before the MFMAs so
   // several HBM round trips overlap.  Elements at or past ke read as zero.
-  constexpr int U = NT <= 2 ? 4 : (NT <= 4 ? 2 : 1);
+  constexpr int U = NT <= 2 ? 8 : (NT <= 4 ? 4 : (NT <= 8 ? 2 : 1));
   if constexpr (sizeof(typename Tag::elem) == 2) {
     constexpr int KS = 32;
     const int64_t steps = (D + KS - 1) / KS;
