@@ -20,8 +20,8 @@ __device__ __forceinline__ void store4(elem* dst, int64_t nb, int64_t N, bool ve
   if constexpr (sizeof(elem) == 2) {
     if (vec4 && nb + 4 <= N) {
       uint2 pk;
-      pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-      pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+      pk.x = f32x2_to_bf16x2_bits(v[0], v[1]);
+      pk.y = f32x2_to_bf16x2_bits(v[2], v[3]);
       *reinterpret_cast<uint2*>(dst + nb) = pk;
     } else {
 #pragma unroll
@@ -74,7 +74,10 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, const RowCtx& rc, i
         g += bias[n];
         u += bias[a.up_off + n];
       }
-      v[i] = g / (1.f + __expf(-g)) * u;
+      // silu(g) = g / (1 + e^-g), with e^-g = 2^(-g log2 e) and the
+      // hardware reciprocal (about 1 ulp each, far below the bf16 rounding
+      // of h that follows)
+      v[i] = g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * g)) * u;
     } else if constexpr (EPI == EPI_RELU) {
       float t = acc0[i];
       if (bias && ok) t += bias[n];

@@ -240,8 +240,8 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
       }
       if (a.out_bf16) {
         uint2 pk;
-        pk.x = f32_to_bf16_bits(s.x) | (f32_to_bf16_bits(s.y) << 16);
-        pk.y = f32_to_bf16_bits(s.z) | (f32_to_bf16_bits(s.w) << 16);
+        pk.x = f32x2_to_bf16x2_bits(s.x, s.y);
+        pk.y = f32x2_to_bf16x2_bits(s.z, s.w);
         reinterpret_cast<uint2*>(a.out)[i] = pk;
       } else {
         reinterpret_cast<float4*>(a.out)[i] = s;

@@ -24,12 +24,17 @@ struct BF16 {
 // ---------------------------------------------------------------- numerics
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Round-to-nearest-even float -> bf16 bits (NaN stays NaN).
+// float -> bf16 bits, rounded to nearest even by gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32; a NaN stays a NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Two floats -> packed bf16 bits (a in the low half), one instruction.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
