@@ -82,7 +82,11 @@ __device__ void build_work_lists(const DispatchArgs& a, const int* cnts, const i
   for (int g = 0; g < a.nspec; ++g) {
     const WorkSpec& sp = a.spec[g];
     __syncthreads();
-    if (tid < E) tst[tid] = (cnts[tid] + sp.bm - 1) / sp.bm;
+    // Row tiles per expert: bm rows each, the last one taking up to xr more.
+    if (tid < E) {
+      const int c = cnts[tid];
+      tst[tid] = c == 0 ? 0 : max(1, (c - sp.xr + sp.bm - 1) / sp.bm);
+    }
     __syncthreads();
     const int tiles = block_exclusive_scan(tst, tmp, E);
     if (tid == 0) tst[E] = tiles;

@@ -86,12 +86,19 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int OUTC = DUAL ? 128 : 256;        // output columns per tile
   constexpr int WN = OUTC / WAVES_N, SN = WN / 32;  // 32-column MFMA tiles per wave (per half)
   constexpr int NACC = DUAL ? 2 : 1;
-  constexpr int AB = BM * KB;                   // A bytes per stage
+  // The ping-pong tile holds up to XRC rows past BM: an expert's last tile
+  // takes a tail of at most a.tail_rows rows with it (waves 0-3 load those
+  // rows and compute them, see below) instead of leaving it to a nearly
+  // empty tile of its own.
+  constexpr bool PP = S == 2 && NW == 8 && NT == 4 && BM == 256;
+  constexpr int XRC = PP ? kTailRows : 0;
+  constexpr int AB = (BM + XRC) * KB;           // A bytes per stage
   constexpr int STAGE = AB + NBR * KB;
   constexpr int AI = BM / RPI / NW;             // A load instructions per wave per stage
   constexpr int BI = NBR / RPI / NW;            // B load instructions per wave per stage
   constexpr int NI = AI + BI;
   static_assert(AI >= 1 && BI >= 1 && SM >= 1 && SN >= 1, "tile shape");
+  static_assert(XRC == 0 || (XRC == 4 * RPI && XRC == 32 && WAVES_M == 4), "tail strip");
 
   __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
 
@@ -115,7 +122,11 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   }
   const int e = wk.x & 0xff;
   const int r0 = wk.y;
-  const int rows = min(BM, a.offsets[e + 1] - r0);
+  // The last tile of an expert holds its remaining rows when they fit in
+  // BM + tail_rows (the work lists are built with the same rule).
+  const int rem = a.offsets[e + 1] - r0;
+  const int rows = rem <= BM + min(a.tail_rows, XRC) ? rem : BM;
+  const bool xt = XRC > 0 && rows > BM;  // this tile has tail rows
   const int64_t n0 = (int64_t)(wk.x >> 8) * OUTC;
   const int64_t N = a.N;
 
@@ -150,6 +161,14 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     }
     boff[i] = (uint32_t)(wr * a.ldb * 2) + (uint32_t)(((lane % CPR) ^ swz(rB)) * 16);
   }
+  // Tail rows BM..BM+31: wave w < 4 loads rows BM + 8w .. BM + 8w + 7.
+  uint32_t aoffx = 0;
+  if constexpr (XRC > 0) {
+    const int rA = BM + w * RPI + lr;
+    const int r = r0 + (rA < rows ? rA : 0);
+    const int64_t src = a.a_index ? (int64_t)a.a_index[r] : (int64_t)r;
+    aoffx = (uint32_t)(src * a.lda * 2) + (uint32_t)(((lane % CPR) ^ swz(rA)) * 16);
+  }
   const char* Abase = static_cast<const char*>(a.A);
   const char* Bbase = static_cast<const char*>(a.B) + (int64_t)e * a.b_estride * 2;
 
@@ -167,6 +186,8 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < BI; ++i)
       lds_dma16(Bbase + (boff[i] + kb), dst + AB + (w * BI + i) * 1024);
+    if constexpr (XRC > 0)
+      if (xt && w < XRC / RPI) lds_dma16(Abase + (aoffx + kb), dst + (BM / RPI + w) * 1024);
   };
 
   // v_mfma_f32_32x32x16_bf16 with the weights as operand 0: for a 32x32
@@ -180,6 +201,11 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     for (int mi = 0; mi < SM; ++mi)
 #pragma unroll
       for (int ni = 0; ni < SN; ++ni) acc[q][mi][ni] = f32x16{};
+  // Tail strip (rows BM.., 32 of them) of waves 0-3: two 32x32 blocks each.
+  // SwiGLU: the gate and up blocks of h columns wn*WN + 32*wm ..; otherwise
+  // output column blocks 2*wm and 2*wm + 1 of the wave's WN columns.  Both
+  // use B fragments the wave already holds.
+  f32x16 accx[2] = {f32x16{}, f32x16{}};
 
   const int l32 = lane & 31, h = lane >> 5;
   // Fragment addresses (bytes inside a stage): row*KB + swizzled chunk; the
@@ -241,6 +267,29 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
             acc[j / SN][mi][j % SN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[u][j], fa[u][mi],
                                                                             acc[j / SN][mi][j % SN], 0, 0, 0);
     };
+    bf16x8 fx[2];
+    auto memread_x = [&](const char* buf, int hs) {
+      if constexpr (XRC > 0) {
+        if (!xt) return;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          fx[u] = *reinterpret_cast<const bf16x8*>(buf + (BM + l32) * KB + co[2 * hs + u]);
+      }
+    };
+    auto mma_x = [&]() {
+      if constexpr (XRC > 0) {
+        if (!xt) return;
+        // B fragment indices of the two blocks for wm = 0; wm = 1 adds DJ
+        constexpr int J0 = 0, J1 = DUAL ? SN : 1, DJ = DUAL ? 1 : 2;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 b0 = wm ? fb[u][J0 + DJ] : fb[u][J0];
+          const bf16x8 b1 = wm ? fb[u][J1 + DJ] : fb[u][J1];
+          accx[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, fx[u], accx[0], 0, 0, 0);
+          accx[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, fx[u], accx[1], 0, 0, 0);
+        }
+      }
+    };
     auto phase_end = [&](bool loads) {
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's fragment reads have landed
       if (loads) wait_vm<0>();
@@ -256,12 +305,16 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         const char* buf = lds + (k & 1) * STAGE;
         if (k + 1 < ke0) issue(k + 1);
         memread(buf, 0);
+        memread_x(buf, 0);
         phase_end(false);
         mma();
+        mma_x();
         phase_end(false);
         memread(buf, 1);
+        memread_x(buf, 1);
         phase_end(false);
         mma();
+        mma_x();
         phase_end(true);
       }
     } else {
@@ -331,6 +384,10 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     wait_vm<0>();  // no LDS DMA may outlive the workgroup
   }
 
+  // Output column (tile-local) of tail block i of this wave; SwiGLU's two
+  // blocks are the gate and up sums of the same h columns.
+  auto xcol = [&](int i) { return wn * WN + 32 * (DUAL ? wm : 2 * wm + i); };
+  const bool xw = xt && w < 4;  // this wave holds tail-row sums
   if constexpr (SPLITTABLE) {
     if (split_slot >= 0) {
       // raw fp32 partial sums of this K range, tile-local rows x 256 columns
@@ -351,6 +408,20 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
               *reinterpret_cast<float4*>(dst + m * kSplitTileCols + c) =
                   float4{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
             }
+      }
+      if constexpr (XRC > 0) {
+        const int m = BM + l32;
+        if (xw && m < rows) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const f32x16& c0 = accx[i];
+              const int c = (DUAL ? i * OUTC : 0) + xcol(i) + 8 * q4 + 4 * h;
+              *reinterpret_cast<float4*>(dst + m * kSplitTileCols + c) =
+                  float4{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
+            }
+        }
       }
       return;
     }
@@ -373,6 +444,22 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         epilogue4<uint16_t, EPI>(a, rc, n0 + wn * WN + ni * 32 + 8 * q4 + 4 * h, v0, v1, bias);
       }
   }
+  if constexpr (XRC > 0) {
+    const int m = BM + l32;
+    if (xw && m < rows) {
+      const RowCtx rc = row_ctx<EPI>(a, r0 + m);
+#pragma unroll
+      for (int i = 0; i < (DUAL ? 1 : 2); ++i)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x16& c0 = accx[i];
+          const f32x16& c1 = accx[DUAL ? 1 : i];
+          const f32x4 v0{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
+          const f32x4 v1{c1[4 * q4], c1[4 * q4 + 1], c1[4 * q4 + 2], c1[4 * q4 + 3]};
+          epilogue4<uint16_t, EPI>(a, rc, n0 + xcol(i) + 8 * q4 + 4 * h, v0, v1, bias);
+        }
+    }
+  }
 }
 
 // Reduction of the split tiles: kFixupBlocksPerTile blocks share the rows of
@@ -393,9 +480,10 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmArgs a) {
   const int2 wk = a.split_tiles[j];
   const int e = wk.x & 0xff;
   const int r0 = wk.y;
-  const int rows = min(a.split_bm, a.offsets[e + 1] - r0);
+  const int rem = a.offsets[e + 1] - r0;
+  const int rows = rem <= a.split_bm + a.tail_rows ? rem : a.split_bm;  // as the GEMM's tiles
   // this block's share of the tile's rows
-  const int rs = (a.split_bm + kFixupBlocksPerTile - 1) / kFixupBlocksPerTile;
+  const int rs = (rows + kFixupBlocksPerTile - 1) / kFixupBlocksPerTile;
   const int m0 = sub * rs, m1 = min(rows, m0 + rs);
   const int64_t n0 = (int64_t)(wk.x >> 8) * OUTC;
   const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;

@@ -22,6 +22,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct GemmPlan {
   int var = VAR_GENERIC;
   int32_t bm = 128, cols = 128, ntn = 0, max_work = 0;
+  int32_t xr = 0;  // tail rows an expert's last tile may add (256-row bf16 tile only)
 };
 
 // Compute units the K-split of a GEMM's last round is planned for (the split
@@ -71,6 +72,7 @@ GemmPlan plan_gemm(const moe_desc* d, int64_t M, int64_t N, int64_t Kd, int64_t 
     p.var = mean >= 512 ? VAR_BF16_M256 : (mean >= 64 ? VAR_BF16_M128 : VAR_BF16_M32);
   }
   p.bm = variant_rows(p.var);
+  p.xr = p.var == VAR_BF16_M256 ? kTailRows : 0;
   p.cols = variant_cols(p.var, dual);
   p.ntn = (int32_t)((N + p.cols - 1) / p.cols);
   const int64_t bound = (M + p.bm - 1) / p.bm + d->E;
@@ -267,6 +269,7 @@ moe_status route_and_sort(const moe_desc* d, const RoutePlan& rp, const Layout& 
   const size_t works[2] = {L.work1, L.work2};
   for (int i = 0; i < 2; ++i) {
     da.spec[i].bm = plans[i]->bm;
+    da.spec[i].xr = plans[i]->xr;
     da.spec[i].ntn = plans[i]->ntn;
     da.spec[i].max_work = plans[i]->max_work;
     da.spec[i].work = at<int2>(ws, works[i]);
@@ -361,6 +364,7 @@ moe_status forward_impl(const moe_desc* d, const moe_routing* r, const void* x, 
   g.sorted_slot = at<int32_t>(workspace, L.sorted_slot);
   g.sorted_w = at<float>(workspace, L.sorted_w);
   g.vec_ok = aligned16(x) && aligned16(gate_up_proj) && ((d->D * eb) % 16 == 0);
+  g.tail_rows = L.g1.xr;
   const int32_t ncu = (L.split1 || L.split2) ? device_cus() : 0;
   if (L.split1) {
     g.split_tiles = at<int2>(workspace, L.split_tiles1);
@@ -391,6 +395,7 @@ moe_status forward_impl(const moe_desc* d, const moe_routing* r, const void* x, 
   h.num_work = at<int32_t>(workspace, L.num_work) + 1;
   h.max_work = L.g2.max_work;
   h.vec_ok = aligned16(down_proj) && ((d->F * eb) % 16 == 0);
+  h.tail_rows = L.g2.xr;
   h.split_tiles = nullptr;
   h.split_info = nullptr;
   h.partial = nullptr;

@@ -103,6 +103,7 @@ hipError_t launch_capacity(const CapacityArgs& a, hipStream_t s);
 // order; the GEMM grid is sized by max_work and blocks b >= *num_work exit.
 struct WorkSpec {
   int32_t bm;        // rows per tile
+  int32_t xr;        // tail rows an expert's last tile may add (0 or kTailRows)
   int32_t ntn;       // column tiles
   int32_t max_work;  // upper bound of the item count (grid size)
   int2* work;        // (max_work) {expert | column_tile << 8, first sorted row}
@@ -176,17 +177,23 @@ struct GemmArgs {
   int32_t vec_ok;           // rows 16-byte aligned: vector loads allowed
   // K-split items (256- and 32-row bf16 tiles, any epilogue but the atomic
   // combine): the partial sums of part p of split tile j go to partial +
-  // (j*P + p) tiles of 256 x 256 fp32, reduced by launch_split_fixup.
+  // (j*P + p) tiles of kSplitTileRows x kSplitTileCols fp32, reduced by
+  // launch_split_fixup.
   const int2* split_tiles;
   const int32_t* split_info;
   float* partial;
   int32_t split_bm;         // rows per split tile (the kernel variant's tile height)
+  // Rows past BM that an expert's last tile may hold (0, or kTailRows for the
+  // 256-row bf16 tile): a tile whose remaining segment has at most
+  // BM + tail_rows rows takes all of them.  Must match the work lists.
+  int32_t tail_rows;
 };
 hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s);
 // Sums the K parts of every split tile in part order and applies the tile's
 // epilogue `epi` (SwiGLU, ReLU or the down projection's slot store) to the
 // sums.  Four blocks per tile slot, `ncu` slots; blocks past R's exit.
-constexpr int kSplitTileRows = 256, kSplitTileCols = 256;
+constexpr int kTailRows = 32;
+constexpr int kSplitTileRows = 256 + kTailRows, kSplitTileCols = 256;
 hipError_t launch_split_fixup(int epi, const GemmArgs& a, int32_t ncu, hipStream_t s);
 hipError_t launch_gemm_bf16(int epi, int var, const GemmArgs& a, hipStream_t s);
 

@@ -371,3 +371,28 @@ def test_prefill_replay_full_size_sampled():
     st = compare(inp, g, ref, tokens=tok)
     np.testing.assert_array_equal(g["sel"][mask], record[mask])
     _say("err %g exempt %d" % (st, ex))
+
+
+# ------------------------------------------------- tail rows of the last tile
+@pytest.mark.parametrize("act,F,deterministic", [
+    ("swiglu", 320, True),     # every item K-split (30 and 10 items), fix-up over 288-row tiles
+    ("swiglu", 4096, False),   # full rounds plus split parts; atomic combine (no split)
+    ("relu", 4096, True),      # one weight block per output column block
+])
+def test_tail_rows_join_last_tile(act, F, deterministic):
+    """Replay fixes the expert counts at 800 = 3*256 + 32 (the tail joins the
+    last 256-row tile), 545 = 2*256 + 33 (one row too many: a tile of its own),
+    288 (a single tile) and 767; the layer must match the oracle exactly as
+    any other routing does."""
+    T, D, E, K = 1200, 256, 4, 2
+    counts = [800, 545, 288, 767]
+    labels = np.repeat(np.arange(E), counts)
+    record = np.stack([labels[:T], labels[T:]], axis=1)
+    assert np.all(record[:, 0] != record[:, 1])
+    inp = _cfg(T, D, F, E, K, dtype="bf16", act=act, cfg_id=260 + F % 7)
+    _say("tail rows act=%s F=%d deterministic=%s counts=%s" % (act, F, deterministic, counts))
+    g = run_gpu(inp, replay=record, deterministic=deterministic)
+    np.testing.assert_array_equal(g["counts"], counts)
+    ref, _ = reference(inp, g, replay=record)
+    st = compare(inp, g, ref)
+    _say("err %g" % st)
