@@ -82,10 +82,34 @@ __device__ void build_work_lists(const DispatchArgs& a, const int* cnts, const i
   for (int g = 0; g < a.nspec; ++g) {
     const WorkSpec& sp = a.spec[g];
     __syncthreads();
-    // Row tiles per expert: bm rows each, the last one taking up to xr more.
+    // Row tiles per expert: bm rows each; with tail rows (xr) the last one
+    // takes up to xr more.  Tail rows make the last tile of an expert dearer
+    // (one more 32-row strip), so they are used only when they lower the
+    // estimated makespan: full rounds on ncu CUs plus the last partial round
+    // (a K-split part's share when that round is split, else a whole tile).
+    bool tails = false;
+    if (sp.xr > 0 && sp.ncu > 0) {
+      if (tid < E) tst[tid] = (cnts[tid] + sp.bm - 1) / sp.bm;
+      __syncthreads();
+      const int plain = block_exclusive_scan(tst, tmp, E) * sp.ntn;
+      if (tid < E) {
+        const int c = cnts[tid];
+        tst[tid] = c == 0 ? 0 : max(1, (c - sp.xr + sp.bm - 1) / sp.bm);
+      }
+      __syncthreads();
+      const int fused = block_exclusive_scan(tst, tmp, E) * sp.ntn;
+      auto rounds = [&](int total) {
+        const int R = total % sp.ncu;
+        int P = 1;
+        if (sp.split_ncu > 0 && R > 0) P = min(4, sp.split_ncu / R);
+        return (float)(total / sp.ncu) + (R == 0 ? 0.f : (P >= 2 ? 1.f / P : 1.f));
+      };
+      tails = rounds(fused) < rounds(plain);
+    }
+    const int xr = tails ? sp.xr : 0;
     if (tid < E) {
       const int c = cnts[tid];
-      tst[tid] = c == 0 ? 0 : max(1, (c - sp.xr + sp.bm - 1) / sp.bm);
+      tst[tid] = c == 0 ? 0 : max(1, (c - xr + sp.bm - 1) / sp.bm);
     }
     __syncthreads();
     const int tiles = block_exclusive_scan(tst, tmp, E);
@@ -116,7 +140,9 @@ __device__ void build_work_lists(const DispatchArgs& a, const int* cnts, const i
         n = (ntn / kColGroup) * kColGroup + r / mt;
         m = r % mt;
       }
-      return make_int2(x | (n << 8), offs[x] + m * sp.bm);
+      // the last tile of an expert with more than bm remaining rows holds them all
+      const bool tail = m == mt - 1 && offs[x + 1] - (offs[x] + m * sp.bm) > sp.bm;
+      return make_int2(x | (n << 8), (offs[x] + m * sp.bm) | (tail ? kTailTile : 0));
     };
     // Items past the last full round of split_ncu blocks are cut along K.
     int R = 0, P = 1;

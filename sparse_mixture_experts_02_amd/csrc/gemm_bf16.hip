@@ -27,6 +27,8 @@
 // Requires K % 64 == 0, 16-byte aligned operands, and operand regions under
 // 4 GiB (32-bit byte offsets); the host routes anything else to the generic
 // kernel.
+#include <type_traits>
+
 #include "gemm_epilogue.h"
 #include "moe_common.h"
 
@@ -86,10 +88,10 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int OUTC = DUAL ? 128 : 256;        // output columns per tile
   constexpr int WN = OUTC / WAVES_N, SN = WN / 32;  // 32-column MFMA tiles per wave (per half)
   constexpr int NACC = DUAL ? 2 : 1;
-  // The ping-pong tile holds up to XRC rows past BM: an expert's last tile
-  // takes a tail of at most a.tail_rows rows with it (waves 0-3 load those
-  // rows and compute them, see below) instead of leaving it to a nearly
-  // empty tile of its own.
+  // The ping-pong tile holds up to XRC rows past BM: an expert's last tile,
+  // flagged kTailTile in the work list, takes its tail with it instead of
+  // leaving it to a nearly empty tile of its own.  The tail is cut into
+  // 32-row strips; strip g is loaded and computed by wave group g (see below).
   constexpr bool PP = S == 2 && NW == 8 && NT == 4 && BM == 256;
   constexpr int XRC = PP ? kTailRows : 0;
   constexpr int AB = (BM + XRC) * KB;           // A bytes per stage
@@ -98,7 +100,8 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int BI = NBR / RPI / NW;            // B load instructions per wave per stage
   constexpr int NI = AI + BI;
   static_assert(AI >= 1 && BI >= 1 && SM >= 1 && SN >= 1, "tile shape");
-  static_assert(XRC == 0 || (XRC == 4 * RPI && XRC == 32 && WAVES_M == 4), "tail strip");
+  // one or two 32-row strips: wave w loads rows BM + 8w .. (NW * RPI = 64)
+  static_assert(XRC == 0 || ((XRC == 32 || XRC == 64) && NW * RPI == 64 && WAVES_M == 4), "tail strips");
 
   __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
 
@@ -121,18 +124,19 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     }
   }
   const int e = wk.x & 0xff;
-  const int r0 = wk.y;
-  // The last tile of an expert holds its remaining rows when they fit in
-  // BM + tail_rows (the work lists are built with the same rule).
+  const int r0 = wk.y & 0x7fffffff;
+  // A tile flagged kTailTile holds all of its expert's remaining rows (at
+  // most BM + XRC by construction of the work lists; clamped all the same).
   const int rem = a.offsets[e + 1] - r0;
-  const int rows = rem <= BM + min(a.tail_rows, XRC) ? rem : BM;
-  const bool xt = XRC > 0 && rows > BM;  // this tile has tail rows
+  const int rows = min(rem, (wk.y & kTailTile) ? BM + XRC : BM);
   const int64_t n0 = (int64_t)(wk.x >> 8) * OUTC;
   const int64_t N = a.N;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w / WAVES_N, wn = w % WAVES_N;
+  const int grp = w >> 2;                          // wave group of the ping-pong tile
+  const bool xt = XRC > 0 && rows > BM + 32 * grp;  // this group's tail strip has rows
 
   // Load assignment: instruction i of wave w fills LDS rows RPI*(w*XI+i) ..;
   // lane l writes physical chunk l%CPR of row r = RPI*(..)+l/CPR, which holds
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     }
     boff[i] = (uint32_t)(wr * a.ldb * 2) + (uint32_t)(((lane % CPR) ^ swz(rB)) * 16);
   }
-  // Tail rows BM..BM+31: wave w < 4 loads rows BM + 8w .. BM + 8w + 7.
+  // Tail rows BM..BM+63: wave w loads rows BM + 8w .. BM + 8w + 7 (strip w/4).
   uint32_t aoffx = 0;
   if constexpr (XRC > 0) {
     const int rA = BM + w * RPI + lr;
@@ -177,7 +181,10 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   // issues the same number of loads and the wait count is one constant.
   // kb0 <= nk - 1 always, so `klast` is a valid step even for an empty range.
   const int klast = ke0 - 1 > kb0 ? ke0 - 1 : kb0;
-  auto issue = [&](int kt) {
+  // XT_: std::true_type when the tile's tail strips are loaded too (the
+  // flag is a compile-time constant so that tiles without tail rows run the
+  // plain loop).
+  auto issue = [&](int kt, auto XT_) {
     char* dst = lds + (kt % S) * STAGE;
     const uint32_t kb = (uint32_t)min(kt, klast) * (uint32_t)KB;
 #pragma unroll
@@ -186,9 +193,10 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < BI; ++i)
       lds_dma16(Bbase + (boff[i] + kb), dst + AB + (w * BI + i) * 1024);
-    if constexpr (XRC > 0)
-      if (xt && w < XRC / RPI) lds_dma16(Abase + (aoffx + kb), dst + (BM / RPI + w) * 1024);
+    if constexpr (XRC > 0 && decltype(XT_)::value)
+      if (xt) lds_dma16(Abase + (aoffx + kb), dst + (BM / RPI + w) * 1024);
   };
+  constexpr std::false_type kNoTail{};
 
   // v_mfma_f32_32x32x16_bf16 with the weights as operand 0: for a 32x32
   // tile, lane l holds output row (token) l%32 and columns 8q + 4(l/32) + r,
@@ -201,10 +209,11 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     for (int mi = 0; mi < SM; ++mi)
 #pragma unroll
       for (int ni = 0; ni < SN; ++ni) acc[q][mi][ni] = f32x16{};
-  // Tail strip (rows BM.., 32 of them) of waves 0-3: two 32x32 blocks each.
-  // SwiGLU: the gate and up blocks of h columns wn*WN + 32*wm ..; otherwise
-  // output column blocks 2*wm and 2*wm + 1 of the wave's WN columns.  Both
-  // use B fragments the wave already holds.
+  // Tail strip g (rows BM + 32g .. +32) of wave group g: two 32x32 blocks per
+  // wave.  With wg = wm - 2g (0 or 1): SwiGLU, the gate and up blocks of h
+  // columns wn*WN + 32*wg ..; otherwise output column blocks 2*wg and
+  // 2*wg + 1 of the wave's WN columns.  Both use B fragments the wave
+  // already holds.
   f32x16 accx[2] = {f32x16{}, f32x16{}};
 
   const int l32 = lane & 31, h = lane >> 5;
@@ -244,7 +253,6 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     //                     for their loads of stage k+1 before the barrier
     // Stage k's buffer is last read in phase 3 of stage k, so the loads of
     // stage k+2 into it (issued in phase 0/1 of stage k+1) follow a barrier.
-    const int grp = w >> 2;
     bf16x8 fa[2][SM], fb[2][NB];
     auto memread = [&](const char* buf, int hs) {
       if (!busy) return;
@@ -256,38 +264,42 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         for (int mi = 0; mi < SM; ++mi) fa[u][mi] = rdA(buf, 2 * hs + u, mi);
       }
     };
-    auto mma = [&]() {
+    bf16x8 fx[2];
+    // The MFMAs of a half stage.  With the tail strip (XT), its two blocks
+    // follow the first and the last row strip of each slice, so that the
+    // dependent MFMAs on one tail accumulator are several MFMAs apart.
+    auto mma = [&](auto XT_) {
       if (!busy) return;
+      constexpr bool XT = XRC > 0 && decltype(XT_)::value;
+      // B fragment indices of the two tail blocks for wg = 0; wg = 1 adds DJ
+      constexpr int J0 = 0, J1 = DUAL ? SN : 1, DJ = DUAL ? 1 : 2;
+      const bool wg = wm & 1;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int mi = 0; mi < SM; ++mi)
+        for (int mi = 0; mi < SM; ++mi) {
 #pragma unroll
           for (int j = 0; j < NB; ++j)
             acc[j / SN][mi][j % SN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[u][j], fa[u][mi],
                                                                             acc[j / SN][mi][j % SN], 0, 0, 0);
+          if constexpr (XT) {
+            if (mi == 0) {
+              const bf16x8 b0 = wg ? fb[u][J0 + DJ] : fb[u][J0];
+              accx[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, fx[u], accx[0], 0, 0, 0);
+            }
+            if (mi == SM - 1) {
+              const bf16x8 b1 = wg ? fb[u][J1 + DJ] : fb[u][J1];
+              accx[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, fx[u], accx[1], 0, 0, 0);
+            }
+          }
+        }
     };
-    bf16x8 fx[2];
-    auto memread_x = [&](const char* buf, int hs) {
-      if constexpr (XRC > 0) {
+    auto memread_x = [&](const char* buf, int hs, auto XT_) {
+      if constexpr (XRC > 0 && decltype(XT_)::value) {
         if (!xt) return;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          fx[u] = *reinterpret_cast<const bf16x8*>(buf + (BM + l32) * KB + co[2 * hs + u]);
-      }
-    };
-    auto mma_x = [&]() {
-      if constexpr (XRC > 0) {
-        if (!xt) return;
-        // B fragment indices of the two blocks for wm = 0; wm = 1 adds DJ
-        constexpr int J0 = 0, J1 = DUAL ? SN : 1, DJ = DUAL ? 1 : 2;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8 b0 = wm ? fb[u][J0 + DJ] : fb[u][J0];
-          const bf16x8 b1 = wm ? fb[u][J1 + DJ] : fb[u][J1];
-          accx[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, fx[u], accx[0], 0, 0, 0);
-          accx[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, fx[u], accx[1], 0, 0, 0);
-        }
+          fx[u] = *reinterpret_cast<const bf16x8*>(buf + (BM + 32 * grp + l32) * KB + co[2 * hs + u]);
       }
     };
     auto phase_end = [&](bool loads) {
@@ -295,43 +307,56 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
       if (loads) wait_vm<0>();
       barrier_lds();
     };
-    issue(kb0);
-    wait_vm<0>();
-    barrier_lds();
     // The two groups run separate straight-line loops (a branch-free body
-    // keeps the fragments in registers); both meet the same barriers.
-    if (grp == 0) {
-      for (int k = kb0; k < ke0; ++k) {
-        const char* buf = lds + (k & 1) * STAGE;
-        if (k + 1 < ke0) issue(k + 1);
-        memread(buf, 0);
-        memread_x(buf, 0);
-        phase_end(false);
-        mma();
-        mma_x();
-        phase_end(false);
-        memread(buf, 1);
-        memread_x(buf, 1);
-        phase_end(false);
-        mma();
-        mma_x();
-        phase_end(true);
+    // keeps the fragments in registers); both meet the same barriers.  Each
+    // loop exists twice: with the tail strips (XT) and without.
+    auto run = [&](auto XT) {
+      issue(kb0, XT);
+      wait_vm<0>();
+      barrier_lds();
+      if (grp == 0) {
+        for (int k = kb0; k < ke0; ++k) {
+          const char* buf = lds + (k & 1) * STAGE;
+          if (k + 1 < ke0) issue(k + 1, XT);
+          memread(buf, 0);
+          memread_x(buf, 0, XT);
+          phase_end(false);
+          mma(XT);
+          phase_end(false);
+          memread(buf, 1);
+          memread_x(buf, 1, XT);
+          phase_end(false);
+          mma(XT);
+          phase_end(true);
+        }
+      } else {
+        for (int k = kb0; k < ke0; ++k) {
+          const char* buf = lds + (k & 1) * STAGE;
+          if (k > kb0) {
+            mma(XT);
+          }
+          phase_end(false);
+          if (k + 1 < ke0) issue(k + 1, XT);
+          memread(buf, 0);
+          memread_x(buf, 0, XT);
+          phase_end(false);
+          mma(XT);
+          phase_end(false);
+          memread(buf, 1);
+          memread_x(buf, 1, XT);
+          phase_end(true);
+        }
+        if (ke0 > kb0) {
+          mma(XT);
+        }
       }
-    } else {
-      for (int k = kb0; k < ke0; ++k) {
-        const char* buf = lds + (k & 1) * STAGE;
-        if (k > kb0) mma();
-        phase_end(false);
-        if (k + 1 < ke0) issue(k + 1);
-        memread(buf, 0);
-        phase_end(false);
-        mma();
-        phase_end(false);
-        memread(buf, 1);
-        phase_end(true);
-      }
-      if (ke0 > kb0) mma();
-    }
+    };
+    // xt differs between the wave groups (a group whose strip is empty runs
+    // the plain loop); both loops meet the same barriers.
+    if (xt)
+      run(std::true_type{});
+    else
+      run(kNoTail);
     wait_vm<0>();  // no LDS DMA may outlive the workgroup
   } else {
     // Other shapes: every wave loads, waits and computes each stage in step.
@@ -374,11 +399,11 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     };
 
 #pragma unroll
-    for (int p = 0; p < S - 1; ++p) issue(kb0 + p);
+    for (int p = 0; p < S - 1; ++p) issue(kb0 + p, kNoTail);
     for (int kt = kb0; kt < ke0; ++kt) {
       wait_vm<(S - 2) * NI>();
       barrier_lds();
-      issue(kt + S - 1);
+      issue(kt + S - 1, kNoTail);
       if (busy) compute(lds + (kt % S) * STAGE);
     }
     wait_vm<0>();  // no LDS DMA may outlive the workgroup
@@ -386,8 +411,8 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 
   // Output column (tile-local) of tail block i of this wave; SwiGLU's two
   // blocks are the gate and up sums of the same h columns.
-  auto xcol = [&](int i) { return wn * WN + 32 * (DUAL ? wm : 2 * wm + i); };
-  const bool xw = xt && w < 4;  // this wave holds tail-row sums
+  auto xcol = [&](int i) { return wn * WN + 32 * (DUAL ? (wm & 1) : 2 * (wm & 1) + i); };
+  const bool xw = xt;  // this wave holds tail-row sums (strip grp)
   if constexpr (SPLITTABLE) {
     if (split_slot >= 0) {
       // raw fp32 partial sums of this K range, tile-local rows x 256 columns
@@ -410,7 +435,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
             }
       }
       if constexpr (XRC > 0) {
-        const int m = BM + l32;
+        const int m = BM + 32 * grp + l32;
         if (xw && m < rows) {
 #pragma unroll
           for (int i = 0; i < 2; ++i)
@@ -445,7 +470,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
       }
   }
   if constexpr (XRC > 0) {
-    const int m = BM + l32;
+    const int m = BM + 32 * grp + l32;
     if (xw && m < rows) {
       const RowCtx rc = row_ctx<EPI>(a, r0 + m);
 #pragma unroll
@@ -479,9 +504,9 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmArgs a) {
   constexpr int OUTC = DUAL ? kSplitTileCols / 2 : kSplitTileCols;
   const int2 wk = a.split_tiles[j];
   const int e = wk.x & 0xff;
-  const int r0 = wk.y;
+  const int r0 = wk.y & 0x7fffffff;
   const int rem = a.offsets[e + 1] - r0;
-  const int rows = rem <= a.split_bm + a.tail_rows ? rem : a.split_bm;  // as the GEMM's tiles
+  const int rows = min(rem, (wk.y & kTailTile) ? a.split_bm + kTailRows : a.split_bm);  // as the GEMM's tiles
   // this block's share of the tile's rows
   const int rs = (rows + kFixupBlocksPerTile - 1) / kFixupBlocksPerTile;
   const int m0 = sub * rs, m1 = min(rows, m0 + rs);

@@ -279,8 +279,6 @@ int variant_cols(int var, bool dual) {
 
 hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s) {
   if (a.max_work <= 0 || a.N <= 0) return hipSuccess;
-  // Only the 256-row bf16 tile holds tail rows (up to kTailRows).
-  if (a.tail_rows != 0 && (var != VAR_BF16_M256 || a.tail_rows != kTailRows)) return hipErrorInvalidValue;
   if (var != VAR_GENERIC) return launch_gemm_bf16(epi, var, a, s);
   return dtype == 1 ? launch_tag<BF16>(epi, a, s) : launch_tag<F32>(epi, a, s);
 }

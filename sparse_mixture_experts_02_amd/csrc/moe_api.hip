@@ -270,6 +270,7 @@ moe_status route_and_sort(const moe_desc* d, const RoutePlan& rp, const Layout& 
   for (int i = 0; i < 2; ++i) {
     da.spec[i].bm = plans[i]->bm;
     da.spec[i].xr = plans[i]->xr;
+    da.spec[i].ncu = plans[i]->xr > 0 ? device_cus() : 0;
     da.spec[i].ntn = plans[i]->ntn;
     da.spec[i].max_work = plans[i]->max_work;
     da.spec[i].work = at<int2>(ws, works[i]);
@@ -364,7 +365,6 @@ moe_status forward_impl(const moe_desc* d, const moe_routing* r, const void* x, 
   g.sorted_slot = at<int32_t>(workspace, L.sorted_slot);
   g.sorted_w = at<float>(workspace, L.sorted_w);
   g.vec_ok = aligned16(x) && aligned16(gate_up_proj) && ((d->D * eb) % 16 == 0);
-  g.tail_rows = L.g1.xr;
   const int32_t ncu = (L.split1 || L.split2) ? device_cus() : 0;
   if (L.split1) {
     g.split_tiles = at<int2>(workspace, L.split_tiles1);
@@ -395,7 +395,6 @@ moe_status forward_impl(const moe_desc* d, const moe_routing* r, const void* x, 
   h.num_work = at<int32_t>(workspace, L.num_work) + 1;
   h.max_work = L.g2.max_work;
   h.vec_ok = aligned16(down_proj) && ((d->F * eb) % 16 == 0);
-  h.tail_rows = L.g2.xr;
   h.split_tiles = nullptr;
   h.split_info = nullptr;
   h.partial = nullptr;

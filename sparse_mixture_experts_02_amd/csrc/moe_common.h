@@ -103,7 +103,11 @@ hipError_t launch_capacity(const CapacityArgs& a, hipStream_t s);
 // order; the GEMM grid is sized by max_work and blocks b >= *num_work exit.
 struct WorkSpec {
   int32_t bm;        // rows per tile
-  int32_t xr;        // tail rows an expert's last tile may add (0 or kTailRows)
+  // Tail rows an expert's last tile may add (0 or kTailRows).  The builder
+  // uses them when that lowers the estimated number of rounds on `ncu`
+  // compute units, and flags such a tile's first row with kTailTile.
+  int32_t xr;
+  int32_t ncu;
   int32_t ntn;       // column tiles
   int32_t max_work;  // upper bound of the item count (grid size)
   int2* work;        // (max_work) {expert | column_tile << 8, first sorted row}
@@ -183,16 +187,16 @@ struct GemmArgs {
   const int32_t* split_info;
   float* partial;
   int32_t split_bm;         // rows per split tile (the kernel variant's tile height)
-  // Rows past BM that an expert's last tile may hold (0, or kTailRows for the
-  // 256-row bf16 tile): a tile whose remaining segment has at most
-  // BM + tail_rows rows takes all of them.  Must match the work lists.
-  int32_t tail_rows;
 };
 hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s);
 // Sums the K parts of every split tile in part order and applies the tile's
 // epilogue `epi` (SwiGLU, ReLU or the down projection's slot store) to the
 // sums.  Four blocks per tile slot, `ncu` slots; blocks past R's exit.
+// A work item {expert | column_tile << 8, first_row | kTailTile} is the last
+// row tile of its expert and holds all of the expert's remaining rows (at most
+// BM + kTailRows; 256-row bf16 tiles only).
 constexpr int kTailRows = 32;
+constexpr int32_t kTailTile = (int32_t)0x80000000;
 constexpr int kSplitTileRows = 256 + kTailRows, kSplitTileCols = 256;
 hipError_t launch_split_fixup(int epi, const GemmArgs& a, int32_t ncu, hipStream_t s);
 hipError_t launch_gemm_bf16(int epi, int var, const GemmArgs& a, hipStream_t s);

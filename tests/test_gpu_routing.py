@@ -374,25 +374,29 @@ def test_prefill_replay_full_size_sampled():
 
 
 # ------------------------------------------------- tail rows of the last tile
-@pytest.mark.parametrize("act,F,deterministic", [
-    ("swiglu", 320, True),     # every item K-split (30 and 10 items), fix-up over 288-row tiles
-    ("swiglu", 4096, False),   # full rounds plus split parts; atomic combine (no split)
-    ("relu", 4096, True),      # one weight block per output column block
+@pytest.mark.parametrize("act,D,F,deterministic", [
+    ("swiglu", 256, 2816, True),    # gate_up: 264 plain items vs 220 with tails; down unchanged
+    ("swiglu", 5632, 2816, False),  # both projections take tails; atomic combine
+    ("relu", 5632, 2816, True),     # ReLU (one weight block per output block), split down
 ])
-def test_tail_rows_join_last_tile(act, F, deterministic):
-    """Replay fixes the expert counts at 800 = 3*256 + 32 (the tail joins the
-    last 256-row tile), 545 = 2*256 + 33 (one row too many: a tile of its own),
-    288 (a single tile) and 767; the layer must match the oracle exactly as
-    any other routing does."""
-    T, D, E, K = 1200, 256, 4, 2
+def test_tail_rows_join_last_tile(act, D, F, deterministic):
+    """Replay fixes the expert counts at 800 = 3*256 + 32 and 288 = 256 + 32
+    (the tail joins the expert's last 256-row tile), 545 = 2*256 + 33 (one
+    row too many: a tile of its own) and 767.  The work lists take the tails
+    when that saves a round on the device's compute units: with 256 CUs the
+    shapes are chosen so that it does (e.g. 22 column tiles: 264 items = one
+    round and a split remainder, against 220 with tails).  The layer must
+    match the oracle as with any other routing."""
+    T, E, K = 1200, 4, 2
     counts = [800, 545, 288, 767]
     labels = np.repeat(np.arange(E), counts)
     record = np.stack([labels[:T], labels[T:]], axis=1)
     assert np.all(record[:, 0] != record[:, 1])
-    inp = _cfg(T, D, F, E, K, dtype="bf16", act=act, cfg_id=260 + F % 7)
-    _say("tail rows act=%s F=%d deterministic=%s counts=%s" % (act, F, deterministic, counts))
+    inp = _cfg(T, D, F, E, K, dtype="bf16", act=act, cfg_id=270 + D % 7)
+    tokens = None if D <= 256 else np.sort(np.random.default_rng(5).choice(T, 96, replace=False))
+    _say("tail rows act=%s D=%d F=%d deterministic=%s counts=%s" % (act, D, F, deterministic, counts))
     g = run_gpu(inp, replay=record, deterministic=deterministic)
     np.testing.assert_array_equal(g["counts"], counts)
-    ref, _ = reference(inp, g, replay=record)
-    st = compare(inp, g, ref)
+    ref, _ = reference(inp, g, tokens=tokens, replay=record)
+    st = compare(inp, g, ref, tokens=tokens)
     _say("err %g" % st)
