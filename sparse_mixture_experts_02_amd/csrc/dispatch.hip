@@ -177,24 +177,31 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DispatchArgs a) {
   __shared__ int cnts[kMaxExperts];
   const int tid = threadIdx.x;
   const int E = a.E;
-  const int J = kScanThreads / E;      // chunk-range lanes per expert
+  const int nch = a.nchunks;
+  // chunk-range lanes per expert (no more than there are chunks)
+  const int J = max(1, min(kScanThreads / E, nch));
   const int e = tid % E, j = tid / E;
   const bool worker = j < J;
-  const int nch = a.nchunks;
   const int cb = worker ? (int)((int64_t)j * nch / J) : 0;
   const int ce = worker ? (int)((int64_t)(j + 1) * nch / J) : 0;
 
   int s = 0;
   for (int b = cb; b < ce; ++b) s += a.chunk_counts[(int64_t)b * E + e];
-  if (worker) part[j * E + e] = s;
+  // Exclusive scan over j of part[j*E + e] for every expert at once: a
+  // Hillis-Steele scan whose strides are multiples of E.
+  const int n = J * E;
+  tmp[tid] = worker ? s : 0;
+  __syncthreads();
+  for (int off = E; off < n; off <<= 1) {
+    const int y = (tid >= off && worker) ? tmp[tid - off] : 0;
+    __syncthreads();
+    if (worker) tmp[tid] += y;
+    __syncthreads();
+  }
+  if (worker) part[tid] = tmp[tid] - s;
   __syncthreads();
   if (tid < E) {
-    int run = 0;
-    for (int jj = 0; jj < J; ++jj) {
-      const int v = part[jj * E + tid];
-      part[jj * E + tid] = run;
-      run += v;
-    }
+    const int run = tmp[(J - 1) * E + tid];  // the expert's count
     offs[tid] = run;  // count, scanned below
     cnts[tid] = run;
     a.counts[tid] = run;

@@ -243,6 +243,22 @@ def test_decode_mixtral_shape_full():
 
 
 @pytest.mark.slow
+def test_one_expert_share_full_size():
+    """One GPU's share under expert sharding: E = K = 1 at the Mixtral D and F
+    (every token goes to the one expert, whose weight p/(p+1e-9) is 1 in
+    fp32), 2080 rows = 8 full 256-row tiles and a 32-row tail, which both
+    projections take into their last row tile (112 and 16 column tiles: one
+    round fewer)."""
+    inp = workloads.generate(workloads.small_config(2080, 4096, 14336, 1, 1, dtype="bf16", cfg_id=960))
+    _say("one expert T=2080 D=4096 F=14336 E=1 K=1 bf16")
+    g = gpu_forward(inp, deterministic=True)
+    check_full_properties(inp, g)
+    assert np.all(g["weights"] == 1.0) and np.all(g["sel"] == 0)
+    st = check(inp, g, tokens=_sample(2080, 24, seed=3))
+    _say(str(st))
+
+
+@pytest.mark.slow
 @pytest.mark.parametrize("name", ["fine", "fine_zero"])
 def test_fine_grained_128_experts_sampled(name):
     inp = _inputs(name)
