@@ -7,15 +7,17 @@
 //   scan    one block: per-expert totals, the exclusive scan into segment
 //           offsets, each chunk's starting row inside every segment, and the
 //           work lists of the grouped GEMMs (empty experts get no item, so
-//           they launch no MFMA work)
-// Assignments whose expert is the sentinel E (dropped by the dynamic
-// threshold or the capacity) take no row.
-//
+//           they launch no MFMA work; whether an expert's last row tile
+//           takes its tail rows is decided here, see build_work_lists)
 //   scatter one block per chunk: the chunk is walked in order; inside a wave
 //           equal experts are found with nine ballots (expert id bits plus a
 //           validity bit) and ranked by popcount, and waves are ordered
 //           through per-wave counts in LDS.  Row order inside a segment is
 //           therefore increasing (t, k).
+//
+// Decode-sized calls (T*K <= 1024) run the three steps in one block of one
+// launch.  Assignments whose expert is the sentinel E (dropped by the
+// dynamic threshold or the capacity) take no row.
 //
 // The host never reads the counts: the GEMM grids are sized by the bound
 // (ceil(T*K / bm) + E) * column tiles on the number of items and surplus

@@ -7,8 +7,10 @@
 // up rows, so 128 h columns; otherwise 256 output columns).  MFMA
 // v_mfma_f32_32x32x16_bf16 with the weights as operand 0, so a lane's
 // accumulators are groups of four consecutive output columns of one row.
-// Prefill tiles (BM 256/128) run 8 waves, two per SIMD, 2 x 4 over the tile;
-// the decode tile (BM 32) runs 4 waves side by side along the weight rows.
+// The 256-row tile runs 8 waves (two per SIMD) as a 4 x 2 grid of 64 x 128
+// wave tiles and can take an expert's tail of up to kTailRows more rows; the
+// 128-row tile runs 4 waves (2 x 2); the decode tile (BM 32) runs 4 waves
+// side by side along the weight rows.
 //
 // Data path: global_load_lds_dwordx4 writes each 16-byte chunk straight from
 // HBM/L2 into LDS (no staging registers).  LDS holds S stages of KB bytes of
@@ -16,8 +18,9 @@
 // bits 1.. of the row index.  gfx950 LDS serves 256 bytes per clock; a
 // 32x32 fragment read (32 rows, two chunks) is conflict-free under this
 // swizzle, while XOR-ing with the low row bits halves its throughput
-// (measured with a probe of the two patterns).  A lane of a load instruction writes LDS byte 16*lane of a
-// block of 1024/KB rows, so it loads the global chunk the swizzle puts there.
+// (measured with a probe of the two patterns).  A lane of a load instruction
+// writes LDS byte 16*lane of a block of 1024/KB rows, so it loads the global
+// chunk the swizzle puts there.
 // The 8-wave prefill tile runs a ping-pong schedule (two wave groups take
 // turns between matrix-core work and LDS/global traffic, four barriers per
 // stage, loads issued a stage ahead); the other shapes issue the loads of a
@@ -68,7 +71,7 @@ struct Shape {
 // tiles two 64 KB stages with 8 waves beat deeper pipelines of 32 KB stages
 // (which need twice the barriers); the decode tile is a weight stream and
 // wants more bytes in flight.
-using ShapeM256 = Shape<256, 8, 4, 128, 2>;  // 2 x 64 KB of LDS
+using ShapeM256 = Shape<256, 8, 4, 128, 2>;  // 2 x 68 KB of LDS (with the tail rows)
 using ShapeM128 = Shape<128, 4, 2, 128, 2>;  // 2 x 48 KB
 using ShapeM32 = Shape<32, 4, 1, 128, 4>;    // 4 x 36 KB
 
@@ -165,7 +168,8 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     }
     boff[i] = (uint32_t)(wr * a.ldb * 2) + (uint32_t)(((lane % CPR) ^ swz(rB)) * 16);
   }
-  // Tail rows BM..BM+63: wave w loads rows BM + 8w .. BM + 8w + 7 (strip w/4).
+  // Tail rows BM .. BM+XRC-1: wave w loads rows BM + 8w .. BM + 8w + 7, of
+  // strip w/4 (a wave whose strip is empty or absent loads nothing).
   uint32_t aoffx = 0;
   if constexpr (XRC > 0) {
     const int rA = BM + w * RPI + lr;
@@ -176,9 +180,10 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   const char* Abase = static_cast<const char*>(a.A);
   const char* Bbase = static_cast<const char*>(a.B) + (int64_t)e * a.b_estride * 2;
 
-  // Loads of stage kt into its buffer; past the end of the K range the last
-  // stage is reloaded (into a buffer nobody reads any more), so every step
-  // issues the same number of loads and the wait count is one constant.
+  // Loads of stage kt into its buffer.  The stepped schedule of the other
+  // shapes issues past the end of the K range: the last stage is then
+  // reloaded (into a buffer nobody reads any more), so every step issues the
+  // same number of loads and its wait count is one constant.
   // kb0 <= nk - 1 always, so `klast` is a valid step even for an empty range.
   const int klast = ke0 - 1 > kb0 ? ke0 - 1 : kb0;
   // XT_: std::true_type when the tile's tail strips are loaded too (the
