@@ -10,9 +10,12 @@
 //    16 tokens as its columns.  The four waves split the model width D into
 //    four ranges (split-K) and their partial sums meet in LDS, so one block
 //    reads its 16 token rows exactly once straight from HBM into registers.
-//  * Selection: L lanes per token (L = E rounded up to a power of two, at most
-//    64), each lane holding up to four experts.  Maximum, sum and the K
-//    top-k rounds are xor-shuffle reductions inside the L-lane group.  The
+//  * Selection: L lanes per token, each lane holding up to PL experts: up to 64
+//    experts, L = E rounded up to a power of two and PL = 1..4 (L <= 64);
+//    more than 64 experts, PL = 8 and L = 16 (E <= 128) or 32 (E <= 256), so
+//    that one wave pass covers several tokens and each reduction has fewer
+//    shuffle steps.  Maximum, sum and the K top-k rounds are xor-shuffle
+//    reductions inside the L-lane group.  The
 //    top-k key packs (probability bits << 32) | (0xffffffff - expert): since
 //    probabilities are >= 0 their bit patterns order like the values, and the
 //    larger key on equal probabilities is the lower expert index.
@@ -170,9 +173,14 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
   float* wbuf = part + 32 * EP;
   int* sbuf = reinterpret_cast<int*>(part + 48 * EP);
 
-  // Softmax and top-k with L lanes per token.
+  // Softmax and top-k with L lanes per token, PL experts per lane.
+  constexpr int PL = NT > 4 ? 8 : 4;
   int L = 1;
-  while (L < E && L < 64) L <<= 1;
+  if constexpr (PL == 4) {
+    while (L < E && L < 64) L <<= 1;
+  } else {
+    while (L * PL < E) L <<= 1;
+  }
   const int per_wave = 64 / L;      // tokens one wave pass covers
   const int j = lane % L;           // lane inside the token's group
   for (int base = 0; base < 4; base += per_wave) {
@@ -181,28 +189,28 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
     const bool active = (slot < 4) && (t0 + tk < a.T);
     const float* lg = part + (active ? tk : w * 4) * EP;
 
-    float lv[4];
+    float lv[PL];
     float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < PL; ++i) {
       const int e = j + i * L;
       lv[i] = (e < E) ? lg[e] : -INFINITY;
       m = fmaxf(m, lv[i]);
     }
     for (int o = L >> 1; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    float ev[4], s = 0.f;
+    float ev[PL], s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < PL; ++i) {
       const int e = j + i * L;
       ev[i] = (e < E) ? expf(lv[i] - m) : 0.f;
       s += ev[i];
     }
     for (int o = L >> 1; o > 0; o >>= 1) s += __shfl_xor(s, o);
 
-    float pr[4];
-    uint64_t key[4];
+    float pr[PL];
+    uint64_t key[PL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < PL; ++i) {
       const int e = j + i * L;
       pr[i] = ev[i] / s;
       key[i] = (e < E) ? (((uint64_t)__float_as_uint(pr[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
@@ -227,12 +235,17 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
     }
 
     float psum = 0.f;
-    int mysel[4] = {0, 0, 0, 0};
-    float myp[4] = {0.f, 0.f, 0.f, 0.f};
+    int mysel[PL];
+    float myp[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      mysel[i] = 0;
+      myp[i] = 0.f;
+    }
     for (int k = 0; k < K; ++k) {
       uint64_t best = key[0];
 #pragma unroll
-      for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+      for (int i = 1; i < PL; ++i) best = key[i] > best ? key[i] : best;
       for (int o = L >> 1; o > 0; o >>= 1) {
         const uint64_t other = shfl_xor_u64(best, o);
         best = other > best ? other : best;
@@ -241,14 +254,16 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
       float p = __uint_as_float((uint32_t)(best >> 32));
       if (e % L == j) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < PL; ++i)
           if (e / L == i) key[i] = 0ull;
       }
       if (a.replay) {
         // p of the recorded expert: lane (e % L) of the group holds it as pr[e / L]
         const int er = covered ? (int)a.replay[t * K + k] : 0;
         const int q = er / L;
-        const float mine = q == 0 ? pr[0] : (q == 1 ? pr[1] : (q == 2 ? pr[2] : pr[3]));
+        float mine = pr[0];
+#pragma unroll
+        for (int i = 1; i < PL; ++i) mine = q == i ? pr[i] : mine;
         const float pe = __shfl(mine, (lane & ~(L - 1)) | (er & (L - 1)));
         if (covered) {
           e = er;
@@ -258,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
       psum += p;
       const int kq = k / L, kr = k % L;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < PL; ++i)
         if (kq == i && kr == j) {
           mysel[i] = e;
           myp[i] = p;
@@ -269,10 +284,10 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
     // of "ESMoE"): a non-leading slot whose renormalised weight is below the
     // threshold is dropped and the kept weights are renormalised.
     const float denom = psum + 1e-9f;
-    float wk[4];
-    bool keep[4];
+    float wk[PL];
+    bool keep[PL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < PL; ++i) {
       const int k = j + i * L;
       wk[i] = a.norm ? myp[i] / denom : myp[i];
       keep[i] = k < K;
@@ -280,19 +295,19 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
     if (a.threshold > 0.f) {
       float ks = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < PL; ++i) {
         const int k = j + i * L;
         if (k > 0 && wk[i] < a.threshold) keep[i] = false;
         if (keep[i]) ks += wk[i];
       }
       for (int o = L >> 1; o > 0; o >>= 1) ks += __shfl_xor(ks, o);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wk[i] = keep[i] ? wk[i] / ks : 0.f;
+      for (int i = 0; i < PL; ++i) wk[i] = keep[i] ? wk[i] / ks : 0.f;
     }
 
     if (active) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < PL; ++i) {
         const int k = j + i * L;
         if (k < K) {
           a.sel64[t * K + k] = mysel[i];
@@ -307,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
       }
       if (a.stats_part) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < PL; ++i) {
           const int e = j + i * L;
           if (e < E) pbuf[tk * EP + e] = pr[i];
         }
