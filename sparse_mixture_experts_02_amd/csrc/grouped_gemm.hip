@@ -205,19 +205,19 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   }
 }
 
-template <typename Tag, int EPI>
+template <typename Tag, int EPI, int BM>
 hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((grouped_gemm_kernel<Tag, EPI, 128, 128>), dim3(a.max_work), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<Tag, EPI, BM, 128>), dim3(a.max_work), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename Tag>
+template <typename Tag, int BM>
 hipError_t launch_tag(int epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
-    case EPI_SWIGLU: return launch_epi<Tag, EPI_SWIGLU>(a, s);
-    case EPI_RELU: return launch_epi<Tag, EPI_RELU>(a, s);
-    case EPI_DOWN_ATOMIC: return launch_epi<Tag, EPI_DOWN_ATOMIC>(a, s);
-    default: return launch_epi<Tag, EPI_DOWN_SLOT>(a, s);
+    case EPI_SWIGLU: return launch_epi<Tag, EPI_SWIGLU, BM>(a, s);
+    case EPI_RELU: return launch_epi<Tag, EPI_RELU, BM>(a, s);
+    case EPI_DOWN_ATOMIC: return launch_epi<Tag, EPI_DOWN_ATOMIC, BM>(a, s);
+    default: return launch_epi<Tag, EPI_DOWN_SLOT, BM>(a, s);
   }
 }
 
@@ -268,19 +268,21 @@ int variant_rows(int var) {
   switch (var) {
     case VAR_BF16_M256: return 256;
     case VAR_BF16_M32: return 32;
+    case VAR_GENERIC_M64: return 64;
     default: return 128;
   }
 }
 
 int variant_cols(int var, bool dual) {
-  if (var == VAR_GENERIC) return 128;
+  if (var == VAR_GENERIC || var == VAR_GENERIC_M64) return 128;
   return dual ? 128 : 256;
 }
 
 hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s) {
   if (a.max_work <= 0 || a.N <= 0) return hipSuccess;
+  if (var == VAR_GENERIC_M64) return dtype == 1 ? launch_tag<BF16, 64>(epi, a, s) : launch_tag<F32, 64>(epi, a, s);
   if (var != VAR_GENERIC) return launch_gemm_bf16(epi, var, a, s);
-  return dtype == 1 ? launch_tag<BF16>(epi, a, s) : launch_tag<F32>(epi, a, s);
+  return dtype == 1 ? launch_tag<BF16, 128>(epi, a, s) : launch_tag<F32, 128>(epi, a, s);
 }
 
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {

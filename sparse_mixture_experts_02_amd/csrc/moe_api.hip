@@ -70,6 +70,12 @@ GemmPlan plan_gemm(const moe_desc* d, int64_t M, int64_t N, int64_t Kd, int64_t 
   if (bf16_ok) {
     const int64_t mean = M / d->E;
     p.var = mean >= 512 ? VAR_BF16_M256 : (mean >= 64 ? VAR_BF16_M128 : VAR_BF16_M32);
+  } else {
+    // Generic kernel: 64-row tiles when 128-row ones would not fill two
+    // rounds of a 256-CU part (a fixed count, so the workspace size does not
+    // depend on the device).
+    const int64_t bound128 = ((M + 127) / 128 + d->E) * ((N + 127) / 128);
+    if (bound128 < 2 * kSplitMaxCU) p.var = VAR_GENERIC_M64;
   }
   p.bm = variant_rows(p.var);
   p.xr = p.var == VAR_BF16_M256 ? kTailRows : 0;

@@ -149,11 +149,12 @@ enum Epilogue { EPI_SWIGLU = 0, EPI_RELU = 1, EPI_DOWN_ATOMIC = 2, EPI_DOWN_SLOT
 
 // Kernel variants of the grouped GEMM.
 //   GENERIC: any K / alignment, fp32 or bf16; 128x128 output tiles, operands
-//            staged through registers into LDS.
+//            staged through registers into LDS (GENERIC_M64: 64-row tiles,
+//            for GEMMs with too few 128-row items to fill two rounds).
 //   BF16_Mxxx: bf16 with K a multiple of 64 and 16-byte aligned rows; LDS
 //            double buffer filled by direct global->LDS loads; xxx rows per
 //            tile (256 and 128 for prefill, 32 for decode-sized segments).
-enum Variant { VAR_GENERIC = 0, VAR_BF16_M256 = 1, VAR_BF16_M128 = 2, VAR_BF16_M32 = 3 };
+enum Variant { VAR_GENERIC = 0, VAR_BF16_M256 = 1, VAR_BF16_M128 = 2, VAR_BF16_M32 = 3, VAR_GENERIC_M64 = 4 };
 int variant_rows(int var);
 int variant_cols(int var, bool dual);
 
