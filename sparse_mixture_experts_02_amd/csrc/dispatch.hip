@@ -63,13 +63,27 @@ __device__ int block_exclusive_scan(int* v, int* tmp, int n) {
   return total;
 }
 
-// Position of work item b in the operand-sharing order: blocks are handed to
-// the 8 XCDs round-robin (b % 8), so XCD x receives one contiguous range of
-// the order and its concurrently running tiles share expert rows and weight
-// column tiles in its L2.  A bijection of [0, total).
-__device__ __forceinline__ int xcd_order(int b, int total) {
+// Position of work item b in the operand-sharing order.  Blocks are handed
+// to the 8 XCDs round-robin (b % 8).  Contiguous: XCD x receives one
+// contiguous range of the order.  Windows: an XCD's 32 CUs run its blocks in
+// rounds of 32, so the order is dealt out in windows of 32 items, XCD x
+// taking windows x, x + 8, x + 16, ...; its 32 concurrently running tiles are
+// then one window of the order (with 8 row tiles per expert, exactly one
+// group of 4 column tiles x 8 row tiles) and share 4 weight column tiles and
+// 8 row tiles of activations in its L2, where contiguous ranges straddle the
+// groups (prefill layer -2..-3.4%; the decode weight stream is 3% slower
+// with windows).  Items past the last whole 256-item round go to the XCDs
+// in contiguous ranges.  A bijection of [0, total).
+__device__ __forceinline__ int xcd_order(int b, int total, bool windows) {
+  const int full = windows ? (total / 256) * 256 : 0;
+  if (b < full) {
+    const int i = b / 8, x = b % 8;
+    return 256 * (i / 32) + 32 * x + i % 32;
+  }
+  b -= full;
+  total -= full;
   const int q = total / 8, r = total % 8, x = b % 8, i = b / 8;
-  return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+  return full + (x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i);
 }
 
 // Work lists of the grouped GEMMs from the per-expert counts `cnts` and
@@ -167,7 +181,7 @@ __device__ void build_work_lists(const DispatchArgs& a, const int* cnts, const i
     // the split parts, which blocks b % 8 spread evenly over the XCDs and
     // which dispatch last.
     for (int b = tid; b < n_items && b < sp.max_work; b += kScanThreads)
-      sp.work[b] = b < F ? item(xcd_order(b, F)) : make_int2(kSplitItem | (b - F), 0);
+      sp.work[b] = b < F ? item(xcd_order(b, F, sp.windows != 0)) : make_int2(kSplitItem | (b - F), 0);
   }
 }
 

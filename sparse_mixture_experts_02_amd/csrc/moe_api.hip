@@ -276,6 +276,7 @@ moe_status route_and_sort(const moe_desc* d, const RoutePlan& rp, const Layout& 
   for (int i = 0; i < 2; ++i) {
     da.spec[i].bm = plans[i]->bm;
     da.spec[i].xr = plans[i]->xr;
+    da.spec[i].windows = plans[i]->var == VAR_BF16_M256 || plans[i]->var == VAR_BF16_M128;
     da.spec[i].ncu = plans[i]->xr > 0 ? device_cus() : 0;
     da.spec[i].ntn = plans[i]->ntn;
     da.spec[i].max_work = plans[i]->max_work;

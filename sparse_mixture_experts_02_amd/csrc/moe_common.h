@@ -121,6 +121,11 @@ struct WorkSpec {
   int32_t split_ncu;
   int2* split_tiles;   // (split_ncu)
   int32_t* split_info; // (2): R, P
+  // Order in which the XCDs take the items: 1, 32-item windows dealt out in
+  // turn (the 256- and 128-row tiles, whose rounds then share operands in
+  // L2); 0, one contiguous range per XCD (the 32-row decode tile, a weight
+  // stream, and the generic kernel).
+  int32_t windows;
 };
 constexpr int kColGroup = 4;  // column tiles per ordering group
 constexpr int32_t kSplitItem = (int32_t)0x80000000;
