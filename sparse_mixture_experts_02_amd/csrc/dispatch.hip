@@ -117,7 +117,7 @@ __device__ void build_work_lists(const DispatchArgs& a, const int* cnts, const i
       auto rounds = [&](int total) {
         const int R = total % sp.ncu;
         int P = 1;
-        if (sp.split_ncu > 0 && R > 0) P = min(4, sp.split_ncu / R);
+        if (sp.split_ncu > 0 && R > 0) P = min(kMaxSplitParts, sp.split_ncu / R);
         return (float)(total / sp.ncu) + (R == 0 ? 0.f : (P >= 2 ? 1.f / P : 1.f));
       };
       tails = rounds(fused) < rounds(plain);
@@ -164,7 +164,7 @@ __device__ void build_work_lists(const DispatchArgs& a, const int* cnts, const i
     int R = 0, P = 1;
     if (sp.split_ncu > 0 && total > 0) {
       R = total % sp.split_ncu;
-      P = R > 0 ? min(4, sp.split_ncu / R) : 1;
+      P = R > 0 ? min(kMaxSplitParts, sp.split_ncu / R) : 1;
       if (P < 2) R = 0, P = 1;
     }
     const int F = total - R;

@@ -114,10 +114,11 @@ struct WorkSpec {
   int32_t* num_work; // (1)
   // Split of the last partial round along K (0: off).  With `split_ncu`
   // compute units and `tiles` items, the R = tiles % split_ncu items past the
-  // last full round are each cut into P = min(4, split_ncu / R) K ranges (when
-  // P >= 2), so they fill one round of shorter blocks.  Such an item in `work`
-  // is {kSplitItem | q, 0} with q = j*P + p: part p of split tile j, whose
-  // {expert | column_tile << 8, first row} is split_tiles[j].
+  // last full round are each cut into P = min(kMaxSplitParts, split_ncu / R)
+  // K ranges (when P >= 2), so they fill one round of shorter blocks.  Such
+  // an item in `work` is {kSplitItem | q, 0} with q = j*P + p: part p of
+  // split tile j, whose {expert | column_tile << 8, first row} is
+  // split_tiles[j].
   int32_t split_ncu;
   int2* split_tiles;   // (split_ncu)
   int32_t* split_info; // (2): R, P
@@ -128,6 +129,7 @@ struct WorkSpec {
   int32_t windows;
 };
 constexpr int kColGroup = 4;  // column tiles per ordering group
+constexpr int kMaxSplitParts = 4;  // K parts per split item at most (8 and 16 measured no faster)
 constexpr int32_t kSplitItem = (int32_t)0x80000000;
 
 struct DispatchArgs {
