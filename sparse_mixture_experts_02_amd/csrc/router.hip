@@ -126,8 +126,124 @@ __device__ __forceinline__ void logits_partial(const RouterArgs& a, int64_t t0, 
   }
 }
 
+// Logits of the layers with more than 64 experts (bf16, D a multiple of 256,
+// 16-byte aligned rows): logits[t,e] = x[t] . router[e] (+ bias[e]) for 64
+// tokens per block, so that the router weights (E x D, 0.5 MB at E = 128,
+// D = 2048) are read once per 64 tokens instead of once per 16.  With NW
+// waves, wave w owns tokens 16 (w % 4) .. +16 of the block and the experts
+// of part w / 4 of the NW / 4 equal parts: MFMA 16x16x32 with the experts as
+// rows and the tokens as columns, as in logits_partial.  The router rows go
+// HBM/L2 -> LDS by direct loads in chunks of 64 elements (128-byte rows,
+// 16-byte chunk index XOR-ed with bits 1..3 of the row), kLogitStages chunks
+// in flight; the token rows go straight into registers.  The sum over D runs
+// in one order per (t, e), so the result does not depend on the grid.
+constexpr int kLogitTokens = 64;
+constexpr int kLogitStages = 4;
+constexpr int kLogitWaves = 8;  // two waves per SIMD: one's LDS reads overlap the other's MFMAs
+
+// One 16-byte chunk from global memory straight into LDS: lane l writes LDS
+// bytes [dst + 16 l, dst + 16 l + 16); dst must be wave-uniform.  (Kept out
+// of the kernel template: the host pass does not accept the builtin there.)
+__device__ __forceinline__ void lds_dma16(const char* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+template <int NT, int NW>
+__global__ __launch_bounds__(NW * 64) void router_logits_kernel(RouterArgs a) {
+  constexpr int EP = NT * 16;
+  constexpr int CHUNK = EP * 128;          // bytes of one chunk (EP rows x 64 elements)
+  constexpr int NI = EP / 8 / NW;          // 1 KB load instructions per wave per chunk
+  constexpr int NTW = NT / (NW / 4);       // 16-expert tiles per wave
+  constexpr int S = kLogitStages;
+  static_assert(NW == 4 || NW == 8, "4 token groups of 16, 1 or 2 expert parts");
+  static_assert(NI >= 1 && NI * NW * 8 == EP, "whole 8-row load instructions per wave");
+  __shared__ __attribute__((aligned(1024))) char lds[S * CHUNK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t D = a.D;
+  const int E = a.E;
+  const int ebase = (w / 4) * NTW * 16;    // this wave's first expert row
+  const int64_t tbase = (int64_t)blockIdx.x * kLogitTokens + (w % 4) * 16;
+  const int64_t tok = min(tbase + (lane & 15), a.T - 1);
+  const uint16_t* xr = static_cast<const uint16_t*>(a.x) + tok * D;
+  const char* R = static_cast<const char*>(a.router);
+  const int g = lane >> 4;
+  auto swz = [](int r) { return (r >> 1) & 7; };
+
+  // Loads of chunk c (elements 64c ..): instruction i of wave w fills LDS
+  // rows 8(w + NW i) .. +8; lane l writes physical 16-byte chunk l%8 of row
+  // 8(w + NW i) + l/8, which holds logical chunk (l%8) ^ swz(row).  Rows past
+  // E repeat row E - 1; their logits are not written.
+  uint32_t roff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r = (w + NW * i) * 8 + (lane >> 3);
+    const int er = r < E ? r : E - 1;
+    roff[i] = (uint32_t)((int64_t)er * D * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+  }
+  const int nch = (int)(D / 64);
+  bf16x8 xa[S][2];
+  // chunk c into stage b = c % S (b passed as a constant)
+  auto issue = [&](int c, int b) {
+    char* dst = lds + b * CHUNK;
+    const uint32_t kb = (uint32_t)c * 128u;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) lds_dma16(R + (roff[i] + kb), dst + (w + NW * i) * 1024);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      xa[b][s] = *reinterpret_cast<const bf16x8*>(xr + (int64_t)c * 64 + s * 32 + 8 * g);
+  };
+  f32x4 acc[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Every step issues one chunk (past the end: the last one again, into a
+  // stage nobody reads), so that S - 2 chunks are always in flight behind
+  // the one awaited and the wait count is a constant.
+  constexpr int LATER = (S - 2) * (NI + 2);  // loads per chunk: NI + 2
+  static_assert(S >= 3 && LATER < 64, "vmcnt is 6 bits");
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p) issue(min(p, nch - 1), p);
+  // Unrolled by S (nch is a multiple of S) so that every register-buffer
+  // index is a constant and the loop body has no exit.
+  for (int c0 = 0; c0 < nch; c0 += S) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const int c = c0 + j;
+      __builtin_amdgcn_s_waitcnt((LATER & 15) | ((LATER >> 4) << 14) | 0x0f70);
+      // Chunk c visible; every wave is done with chunk c - 1.  A plain
+      // s_barrier: __syncthreads would also drain the later chunks' loads.
+      // The memory clobber keeps LDS accesses on their side of it.
+      asm volatile("s_barrier" ::: "memory");
+      issue(min(c + S - 1, nch - 1), (j + S - 1) % S);
+      const char* buf = lds + j * CHUNK;
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const int row = ebase + nt * 16 + (lane & 15);
+          const bf16x8 rb = *reinterpret_cast<const bf16x8*>(buf + row * 128 + (((s * 4 + g) ^ swz(row)) * 16));
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb, xa[j][s], acc[nt], 0, 0, 0);
+        }
+    }
+  }
+  // No LDS write may land after the block ends.
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  // lane: token tbase + lane%16, experts ebase + nt*16 + 4*(lane/16) + i
+  const int64_t t = tbase + (lane & 15);
+  if (t < a.T) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = ebase + nt * 16 + 4 * g + i;
+        if (e < E) a.logits[t * E + e] = acc[nt][i] + (a.router_bias ? a.router_bias[e] : 0.f);
+      }
+  }
+}
+
 template <typename Tag, int NT>
-__global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
+__global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a, int pre) {
   constexpr int EP = NT * 16;
   extern __shared__ float part[];  // [4 waves][16 tokens][EP]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -148,23 +264,41 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
     }
   }
 
-  f32x4 acc[NT];
-  logits_partial<Tag, NT>(a, t0, w, lane, acc);
+  if (pre) {
+    // Logits (with the bias) written by router_logits_kernel: all of a
+    // thread's loads issued before the first is awaited.
+    constexpr int PER = 16 * EP / kThreads;
+    float v[PER];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+    for (int q = 0; q < PER; ++q) {
+      // in-bounds address for every lane (no branch around the load)
+      const int idx = tid + q * kThreads, tk = idx / EP, e = idx % EP;
+      const bool ok = e < E && t0 + tk < a.T;
+      const float lv = a.logits[min(t0 + tk, a.T - 1) * E + min(e, E - 1)];
+      v[q] = ok ? lv : 0.f;
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[(w * 16 + (lane & 15)) * EP + nt * 16 + 4 * (lane >> 4) + i] = acc[nt][i];
-  __syncthreads();
+    for (int q = 0; q < PER; ++q) part[tid + q * kThreads] = v[q];
+    __syncthreads();
+  } else {
+    f32x4 acc[NT];
+    logits_partial<Tag, NT>(a, t0, w, lane, acc);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[(w * 16 + (lane & 15)) * EP + nt * 16 + 4 * (lane >> 4) + i] = acc[nt][i];
+    __syncthreads();
 
-  // Sum the four partials; add the bias; publish the logits.
-  for (int idx = tid; idx < 16 * EP; idx += kThreads) {
-    const int tk = idx / EP, e = idx % EP;
-    float v = part[idx] + part[16 * EP + idx] + part[32 * EP + idx] + part[48 * EP + idx];
-    if (e < E && a.router_bias) v += a.router_bias[e];
-    part[idx] = v;
-    if (a.logits && e < E && t0 + tk < a.T) a.logits[(t0 + tk) * E + e] = v;
+    // Sum the four partials; add the bias; publish the logits.
+    for (int idx = tid; idx < 16 * EP; idx += kThreads) {
+      const int tk = idx / EP, e = idx % EP;
+      float v = part[idx] + part[16 * EP + idx] + part[32 * EP + idx] + part[48 * EP + idx];
+      if (e < E && a.router_bias) v += a.router_bias[e];
+      part[idx] = v;
+      if (a.logits && e < E && t0 + tk < a.T) a.logits[(t0 + tk) * E + e] = v;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // Regions of `part` free after the sum above: p (16 x EP), and the
   // weights and experts of the 16 tokens' K slots (16 x K, K <= EP), read
@@ -175,16 +309,18 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
 
   // Softmax and top-k with L lanes per token, PL experts per lane.
   constexpr int PL = NT > 4 ? 8 : 4;
+  // L is a power of two: divisions by it are shifts by lgL.
   int L = 1;
   if constexpr (PL == 4) {
     while (L < E && L < 64) L <<= 1;
   } else {
     while (L * PL < E) L <<= 1;
   }
-  const int per_wave = 64 / L;      // tokens one wave pass covers
-  const int j = lane % L;           // lane inside the token's group
+  const int lgL = __builtin_ctz(L);
+  const int per_wave = 64 >> lgL;   // tokens one wave pass covers
+  const int j = lane & (L - 1);     // lane inside the token's group
   for (int base = 0; base < 4; base += per_wave) {
-    const int slot = base + lane / L;          // 0..3 inside this wave's four tokens
+    const int slot = base + (lane >> lgL);     // 0..3 inside this wave's four tokens
     const int tk = w * 4 + slot;
     const bool active = (slot < 4) && (t0 + tk < a.T);
     const float* lg = part + (active ? tk : w * 4) * EP;
@@ -252,15 +388,15 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
       }
       int e = (int)(0xffffffffu - (uint32_t)best);
       float p = __uint_as_float((uint32_t)(best >> 32));
-      if (e % L == j) {
+      if ((e & (L - 1)) == j) {
 #pragma unroll
         for (int i = 0; i < PL; ++i)
-          if (e / L == i) key[i] = 0ull;
+          if ((e >> lgL) == i) key[i] = 0ull;
       }
       if (a.replay) {
         // p of the recorded expert: lane (e % L) of the group holds it as pr[e / L]
         const int er = covered ? (int)a.replay[t * K + k] : 0;
-        const int q = er / L;
+        const int q = er >> lgL;
         float mine = pr[0];
 #pragma unroll
         for (int i = 1; i < PL; ++i) mine = q == i ? pr[i] : mine;
@@ -271,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
         }
       }
       psum += p;
-      const int kq = k / L, kr = k % L;
+      const int kq = k >> lgL, kr = k & (L - 1);
 #pragma unroll
       for (int i = 0; i < PL; ++i)
         if (kq == i && kr == j) {
@@ -394,11 +530,22 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   }
 }
 
+// Launches router_logits_kernel when it applies; returns whether it did.
+template <int NT>
+int launch_logits(const RouterArgs& a, hipStream_t s) {
+  if (!(a.vec_ok && a.D % (64 * kLogitStages) == 0 && a.logits)) return 0;
+  const unsigned grid = (unsigned)((a.T + kLogitTokens - 1) / kLogitTokens);
+  hipLaunchKernelGGL((router_logits_kernel<NT, kLogitWaves>), dim3(grid), dim3(kLogitWaves * 64), 0, s, a);
+  return 1;
+}
+
 template <typename Tag, int NT>
 hipError_t launch_nt(const RouterArgs& a, hipStream_t s) {
+  int pre = 0;
+  if constexpr (NT >= 8 && Tag::kBytes == 2) pre = launch_logits<NT>(a, s);
   const unsigned grid = (unsigned)((a.T + kRouterTokens - 1) / kRouterTokens);
   const size_t lds = (size_t)4 * 16 * NT * 16 * sizeof(float);
-  hipLaunchKernelGGL((router_kernel<Tag, NT>), dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((router_kernel<Tag, NT>), dim3(grid), dim3(kThreads), lds, s, a, pre);
   return hipGetLastError();
 }
 

@@ -91,6 +91,12 @@ EDGE = [
     (40, 256, 384, 8, 2, "swiglu", "bf16", False, True),
     (64, 4096, 1024, 8, 2, "swiglu", "bf16", False, True),
     (3000, 64, 128, 40, 6, "swiglu", "bf16", False, True),
+    # bf16 routers over more than 64 experts with D a multiple of 256 take the
+    # LDS-staged logits kernel (64 tokens per block): ragged token blocks,
+    # expert counts off the 16-row MFMA tile, a router bias, 8 and 16 tiles
+    (1000, 512, 128, 128, 8, "swiglu", "bf16", True, True),
+    (70, 256, 64, 100, 6, "swiglu", "bf16", False, True),
+    (300, 768, 64, 200, 4, "relu", "bf16", True, False),
 ]
 
 
