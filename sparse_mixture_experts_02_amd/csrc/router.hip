@@ -533,7 +533,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 // Launches router_logits_kernel when it applies; returns whether it did.
 template <int NT>
 int launch_logits(const RouterArgs& a, hipStream_t s) {
-  if (!(a.vec_ok && a.D % (64 * kLogitStages) == 0 && a.logits)) return 0;
+  // (router offsets are 32-bit byte offsets)
+  if (!(a.vec_ok && a.D % (64 * kLogitStages) == 0 && a.logits && (int64_t)a.E * a.D * 2 < (int64_t)UINT32_MAX))
+    return 0;
   const unsigned grid = (unsigned)((a.T + kLogitTokens - 1) / kLogitTokens);
   hipLaunchKernelGGL((router_logits_kernel<NT, kLogitWaves>), dim3(grid), dim3(kLogitWaves * 64), 0, s, a);
   return 1;
