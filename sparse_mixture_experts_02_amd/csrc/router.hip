@@ -10,6 +10,9 @@
 //    16 tokens as its columns.  The four waves split the model width D into
 //    four ranges (split-K) and their partial sums meet in LDS, so one block
 //    reads its 16 token rows exactly once straight from HBM into registers.
+//    bf16 routers over more than 64 experts take their logits instead from
+//    router_logits_kernel (64 tokens per block, router rows staged in LDS),
+//    launched just before, and this kernel reads them back.
 //  * Selection: L lanes per token, each lane holding up to PL experts: up to 64
 //    experts, L = E rounded up to a power of two and PL = 1..4 (L <= 64);
 //    more than 64 experts, PL = 8 and L = 16 (E <= 128) or 32 (E <= 256), so
