@@ -17,8 +17,9 @@
 //    experts, L = E rounded up to a power of two and PL = 1..4 (L <= 64);
 //    more than 64 experts, PL = 8 and L = 16 (E <= 128) or 32 (E <= 256), so
 //    that one wave pass covers several tokens and each reduction has fewer
-//    shuffle steps.  Maximum, sum and the K top-k rounds are xor-shuffle
-//    reductions inside the L-lane group.  The
+//    exchange steps.  Maximum, sum and the K top-k rounds are reductions
+//    inside the L-lane group: DPP register moves within 16 lanes, ds_bpermute
+//    beyond (see group_reduce).  The
 //    top-k key packs (probability bits << 32) | (0xffffffff - expert): since
 //    probabilities are >= 0 their bit patterns order like the values, and the
 //    larger key on equal probabilities is the lower expert index.
@@ -55,10 +56,39 @@ __device__ __forceinline__ float4 load_f32x4(const float* row, int64_t k, int64_
   return v;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
-  uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+// Reductions over aligned groups of 2^lg lanes, every lane receiving the
+// result.  Step i pairs each lane with one of the other half of its 2^(i+1)
+// group: xor 1 and xor 2 (DPP quad permutations), the mirror inside 8 lanes
+// and the mirror inside 16 lanes (DPP row_half_mirror and row_mirror: lane i
+// with 7 - i and 15 - i), then xor 16 and xor 32 through ds_bpermute.  The
+// first four are register moves, not LDS round trips.  Both lanes of a pair
+// combine the same two values, so with a commutative op every lane of the
+// group ends with the same bits.
+template <int STEP>
+__device__ __forceinline__ int xchg(int v) {
+  if constexpr (STEP == 0) return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  else if constexpr (STEP == 1) return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  else if constexpr (STEP == 2) return __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false); // row_half_mirror
+  else if constexpr (STEP == 3) return __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false); // row_mirror
+  else return __shfl_xor(v, 1 << STEP);
+}
+template <int STEP>
+__device__ __forceinline__ float xchg(float v) { return __int_as_float(xchg<STEP>(__float_as_int(v))); }
+template <int STEP>
+__device__ __forceinline__ uint64_t xchg(uint64_t v) {
+  const uint32_t lo = (uint32_t)xchg<STEP>((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)xchg<STEP>((int)(uint32_t)(v >> 32));
   return ((uint64_t)hi << 32) | lo;
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T group_reduce(T v, int lg, Op op) {
+  if (lg > 0) v = op(v, xchg<0>(v));
+  if (lg > 1) v = op(v, xchg<1>(v));
+  if (lg > 2) v = op(v, xchg<2>(v));
+  if (lg > 3) v = op(v, xchg<3>(v));
+  if (lg > 4) v = op(v, xchg<4>(v));
+  if (lg > 5) v = op(v, xchg<5>(v));
+  return v;
 }
 
 // Partial logits of this wave's D range: acc[nt][i] = sum over the range of
@@ -336,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a, int pre)
       lv[i] = (e < E) ? lg[e] : -INFINITY;
       m = fmaxf(m, lv[i]);
     }
-    for (int o = L >> 1; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    m = group_reduce(m, lgL, [](float u, float v) { return fmaxf(u, v); });
     float ev[PL], s = 0.f;
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
@@ -344,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a, int pre)
       ev[i] = (e < E) ? expf(lv[i] - m) : 0.f;
       s += ev[i];
     }
-    for (int o = L >> 1; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    s = group_reduce(s, lgL, [](float u, float v) { return u + v; });
 
     float pr[PL];
     uint64_t key[PL];
@@ -369,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a, int pre)
           bad |= (e < 0 || e >= E) ? 1 : 0;
         }
       }
-      for (int o = L >> 1; o > 0; o >>= 1) bad |= __shfl_xor(bad, o);
+      bad = group_reduce(bad, lgL, [](int u, int v) { return u | v; });
       covered = active && !bad && (!a.replay_mask || a.replay_mask[t] != 0);
     }
 
@@ -385,10 +415,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a, int pre)
       uint64_t best = key[0];
 #pragma unroll
       for (int i = 1; i < PL; ++i) best = key[i] > best ? key[i] : best;
-      for (int o = L >> 1; o > 0; o >>= 1) {
-        const uint64_t other = shfl_xor_u64(best, o);
-        best = other > best ? other : best;
-      }
+      best = group_reduce(best, lgL, [](uint64_t u, uint64_t v) { return u > v ? u : v; });
       int e = (int)(0xffffffffu - (uint32_t)best);
       float p = __uint_as_float((uint32_t)(best >> 32));
       if ((e & (L - 1)) == j) {
@@ -439,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a, int pre)
         if (k > 0 && wk[i] < a.threshold) keep[i] = false;
         if (keep[i]) ks += wk[i];
       }
-      for (int o = L >> 1; o > 0; o >>= 1) ks += __shfl_xor(ks, o);
+      ks = group_reduce(ks, lgL, [](float u, float v) { return u + v; });
 #pragma unroll
       for (int i = 0; i < PL; ++i) wk[i] = keep[i] ? wk[i] / ks : 0.f;
     }
