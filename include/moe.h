@@ -226,6 +226,25 @@ moe_status moe_dispatch_routed(const moe_desc* d, const moe_routing* r, const vo
 /* Human-readable text of a status code (static storage). */
 const char* moe_status_string(moe_status s);
 
+/* ---- Measurement probes (not part of the layer) --------------------------
+ * Kernels that measure the part's attainable rates, so that the layer's
+ * kernels can be reported against measured ceilings beside the published
+ * peaks.  Asynchronous on `stream`; the caller owns every buffer.
+ *
+ * moe_probe_mfma: `blocks` blocks of 8 waves, each wave issuing `iters`
+ *   rounds of 8 independent v_mfma_f32_32x32x16_bf16 on register operands.
+ *   out: device fp32, blocks * 512 elements (one word per lane, written so
+ *   the work stays live; values meaningless).  MOE_EINVAL if blocks or iters
+ *   <= 0 or out is NULL.
+ * moe_probe_mfma_flops: the FLOPs one such launch performs (0 for bad sizes).
+ * moe_probe_read: `blocks` blocks of 256 threads read `bytes` bytes of the
+ *   device buffer `buf` once, in 16-byte loads, grid-stride.  out: device
+ *   fp32, blocks * 256 elements.  MOE_EINVAL if a pointer is NULL, buf is not
+ *   16-byte aligned, bytes <= 0 or not a multiple of 16, or blocks <= 0. */
+moe_status moe_probe_mfma(int32_t blocks, int32_t iters, float* out, void* stream);
+int64_t moe_probe_mfma_flops(int32_t blocks, int32_t iters);
+moe_status moe_probe_read(const void* buf, int64_t bytes, int32_t blocks, float* out, void* stream);
+
 /* ABI version of this header (bumped on any signature change). */
 int32_t moe_abi_version(void);
 #define MOE_ABI_VERSION 2

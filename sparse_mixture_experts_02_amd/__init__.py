@@ -94,6 +94,12 @@ def load_library():
         lib.moe_status_string.restype = ctypes.c_char_p
         lib.moe_abi_version.argtypes = []
         lib.moe_abi_version.restype = I32
+        lib.moe_probe_mfma.argtypes = [I32, I32, P, P]
+        lib.moe_probe_mfma.restype = ctypes.c_int
+        lib.moe_probe_mfma_flops.argtypes = [I32, I32]
+        lib.moe_probe_mfma_flops.restype = ctypes.c_int64
+        lib.moe_probe_read.argtypes = [P, ctypes.c_int64, I32, P, P]
+        lib.moe_probe_read.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -105,6 +111,20 @@ def moe_status_string(status: int) -> str:
 
 def moe_abi_version() -> int:
     return int(load_library().moe_abi_version())
+
+
+def moe_probe_mfma(blocks, iters, out, stream) -> int:
+    """Raw call of the matrix-core rate probe; returns the status code."""
+    return load_library().moe_probe_mfma(int(blocks), int(iters), out, stream)
+
+
+def moe_probe_mfma_flops(blocks, iters) -> int:
+    return int(load_library().moe_probe_mfma_flops(int(blocks), int(iters)))
+
+
+def moe_probe_read(buf, nbytes, blocks, out, stream) -> int:
+    """Raw call of the HBM read-rate probe; returns the status code."""
+    return load_library().moe_probe_read(buf, int(nbytes), int(blocks), out, stream)
 
 
 def moe_workspace_bytes(desc: MoeDesc) -> int:

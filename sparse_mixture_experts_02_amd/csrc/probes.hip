@@ -1,0 +1,85 @@
+// Measurement probes: kernels that measure this part's attainable matrix-core
+// rate and HBM read rate under the conditions the layer runs in (clock under
+// the power cap, the memory system's real efficiency), so that the layer's
+// kernels can be reported against measured ceilings beside the published ones.
+// They compute nothing of the layer.
+//
+//   mfma_probe: waves issue back-to-back v_mfma_f32_32x32x16_bf16 on register
+//               operands (eight independent accumulators per wave, so that no
+//               MFMA waits on the previous one's result); no memory traffic
+//               but one word per lane at the end, which keeps the work live.
+//   read_probe: a grid-stride read of a buffer in 16-byte loads (consecutive
+//               lanes on consecutive addresses), summed per lane; one word per
+//               lane written at the end.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kProbeWaves = 8;   // per block: two per SIMD, as the prefill GEMM tile
+constexpr int kProbeChains = 8;  // independent accumulators per wave
+
+__global__ __launch_bounds__(kProbeWaves * 64) void mfma_probe_kernel(int iters, float* out) {
+  const int lane = threadIdx.x & 63;
+  bf16x8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (float)(lane + i));
+    b[i] = (__bf16)(0.002f * (float)(lane - i));
+  }
+  f32x16_t acc[kProbeChains];
+#pragma unroll
+  for (int c = 0; c < kProbeChains; ++c) acc[c] = f32x16_t{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kProbeChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kProbeChains; ++c) s += acc[c][0] + acc[c][15];
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void read_probe_kernel(const float4* __restrict__ p, int64_t n4, float* out) {
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    const float4 v = p[i];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc.x + acc.y + acc.z + acc.w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_probe_mfma_flops(int32_t blocks, int32_t iters) {
+  if (blocks <= 0 || iters <= 0) return 0;
+  return (int64_t)blocks * kProbeWaves * iters * kProbeChains * (2LL * 32 * 32 * 16);
+}
+
+moe_status moe_probe_mfma(int32_t blocks, int32_t iters, float* out, void* stream) {
+  if (blocks <= 0 || iters <= 0 || !out) return MOE_EINVAL;
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(kProbeWaves * 64), 0, static_cast<hipStream_t>(stream),
+                     iters, out);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EDEVICE;
+}
+
+moe_status moe_probe_read(const void* buf, int64_t bytes, int32_t blocks, float* out, void* stream) {
+  if (!buf || !out || bytes <= 0 || bytes % 16 != 0 || blocks <= 0) return MOE_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(buf) & 15) != 0) return MOE_EINVAL;
+  hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const float4*>(buf), bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EDEVICE;
+}
+
+}  // extern "C"

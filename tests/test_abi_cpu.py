@@ -156,3 +156,19 @@ def test_python_errors_map(lib):
 def test_bench_refuses_several_gpus():
     r = subprocess.run(["python3", os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_probes_validate_on_the_host(lib):
+    # the FLOP count of a matrix-core probe launch: 8 waves x 8 chains of 32x32x16 MFMAs per round
+    assert moe.moe_probe_mfma_flops(2, 3) == 2 * 8 * 3 * 8 * (2 * 32 * 32 * 16)
+    assert moe.moe_probe_mfma_flops(0, 3) == 0
+    einval = 1
+    # rejected before any launch (no device needed)
+    assert moe.moe_probe_mfma(0, 10, 4096, None) == einval
+    assert moe.moe_probe_mfma(4, 0, 4096, None) == einval
+    assert moe.moe_probe_mfma(4, 10, None, None) == einval
+    assert moe.moe_probe_read(None, 1024, 4, 4096, None) == einval
+    assert moe.moe_probe_read(4096, 1000, 4, 4096, None) == einval   # not a multiple of 16 bytes
+    assert moe.moe_probe_read(4104, 1024, 4, 4096, None) == einval   # buffer not 16-byte aligned
+    assert moe.moe_probe_read(4096, 1024, 0, 4096, None) == einval
+
