@@ -97,6 +97,10 @@ EDGE = [
     (1000, 512, 128, 128, 8, "swiglu", "bf16", True, True),
     (70, 256, 64, 100, 6, "swiglu", "bf16", False, True),
     (300, 768, 64, 200, 4, "relu", "bf16", True, False),
+    # fp32 and non-multiple-of-256 widths over more than 64 experts keep the
+    # logits inside the 16-token router blocks
+    (200, 96, 64, 80, 4, "swiglu", "f32", True, True),
+    (150, 320, 64, 130, 3, "swiglu", "bf16", False, True),
 ]
 
 
