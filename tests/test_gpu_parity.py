@@ -309,6 +309,25 @@ def test_token_permutation_equivariance():
     assert err.max() <= 1e-5 * max(np.abs(ref).max(), 1e-30), err.max()
 
 
+@pytest.mark.parametrize("E,K", [(8, 2), (128, 8)])
+def test_router_is_batch_invariant(E, K):
+    """Both router paths (16-token blocks for up to 64 experts; the logits
+    kernel of 64-token blocks above) sum each (t, e) in one order whatever the
+    batch: a permuted batch and a prefix of it give the same logits,
+    selections and weights bitwise."""
+    inp = workloads.generate(workloads.small_config(1000, 512, 128, E, K, dtype="bf16", router_bias="zipf",
+                                                    cfg_id=952 + E))
+    perm = np.random.default_rng(11).permutation(1000)
+    a = gpu_forward(inp)
+    b = gpu_forward(dict(inp, x=inp["x"][perm]))
+    for k in ("sel", "weights", "logits"):
+        np.testing.assert_array_equal(b[k], a[k][perm])
+    T1 = 300
+    c = gpu_forward(dict(inp, x=inp["x"][:T1], cfg=dict(inp["cfg"], T=T1)))
+    for k in ("sel", "weights", "logits"):
+        np.testing.assert_array_equal(c[k], a[k][:T1])
+
+
 def test_timed_entry_point_matches_forward():
     """moe_forward_timed is moe_forward plus event records: bitwise equal outputs."""
     import ctypes
