@@ -172,7 +172,7 @@ __device__ __forceinline__ void logits_partial(const RouterArgs& a, int64_t t0, 
 // in one order per (t, e), so the result does not depend on the grid.
 constexpr int kLogitTokens = 64;
 constexpr int kLogitStages = 4;
-constexpr int kLogitWaves = 8;  // two waves per SIMD: one's LDS reads overlap the other's MFMAs
+constexpr int kLogitWaves = 8;  // two waves per SIMD (four waves, or eight chunks in flight, measured the same)
 
 // One 16-byte chunk from global memory straight into LDS: lane l writes LDS
 // bytes [dst + 16 l, dst + 16 l + 16); dst must be wave-uniform.  (Kept out
