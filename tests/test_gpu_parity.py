@@ -100,6 +100,8 @@ EDGE = [
     # fp32 and non-multiple-of-256 widths over more than 64 experts keep the
     # logits inside the 16-token router blocks
     (200, 96, 64, 80, 4, "swiglu", "f32", True, True),
+    # more 1024-assignment chunks than the scan has lanes per expert (137 > 128)
+    (70000, 64, 64, 8, 2, "swiglu", "f32", False, True),
     (150, 320, 64, 130, 3, "swiglu", "bf16", False, True),
 ]
 
