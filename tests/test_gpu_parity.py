@@ -134,8 +134,10 @@ def test_random_small_sweep(seed):
     check_full_properties(inp, g)
 
 
-def test_bf16_output():
-    cfg = workloads.small_config(400, 128, 192, 8, 2, dtype="bf16", cfg_id=400)
+@pytest.mark.parametrize("T,D,F,E", [(400, 128, 192, 8), (4000, 256, 512, 4)])
+def test_bf16_output(T, D, F, E):
+    # 128-row tiles; 256-row tiles with tail rows and K-split parts
+    cfg = workloads.small_config(T, D, F, E, 2, dtype="bf16", cfg_id=400 + E)
     inp = workloads.generate(cfg)
     for det in (False, True):
         g = gpu_forward(inp, deterministic=det, out_dtype=torch.bfloat16)
