@@ -24,6 +24,9 @@
  *   - Tensors are contiguous, row-major DEVICE pointers unless stated.  Weights
  *     use the Hugging Face layouts: router (E,D), gate_up_proj (E,G*F,D) with
  *     G=2 for SwiGLU (W1 (E,F,D) with G=1 for ReLU), down_proj (E,D,F).
+ *   - The layer entry points (moe_forward*) read x, gate_up_proj and down_proj
+ *     and use the workspace in 16-byte units: those four pointers must be
+ *     16-byte aligned (MOE_EINVAL otherwise; fresh device allocations are).
  *   - The caller owns every buffer.  The library never writes its inputs,
  *     allocates no device memory and keeps no state; scratch memory is the
  *     caller's workspace, sized by moe_workspace_bytes.

@@ -208,6 +208,13 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _aligned16(t):
+    """t as a contiguous tensor whose data starts on a 16-byte boundary (a copy
+    only when a view starts elsewhere)."""
+    t = t.contiguous()
+    return t if t.data_ptr() % 16 == 0 else t.clone()
+
+
 def make_desc(T, D, F, E, K, *, norm_topk_prob=True, act="silu", dtype=None, out_dtype=None,
               deterministic=False) -> MoeDesc:
     return MoeDesc(T=int(T), D=int(D), F=int(F), E=int(E), K=int(K), norm_topk=int(bool(norm_topk_prob)),
@@ -300,7 +307,11 @@ def forward(x, router, gate_up_proj, down_proj, *, top_k, norm_topk_prob=True, a
     kept = torch.empty((T, top_k), dtype=torch.uint8, device=dev) if return_kept else None
     stats = torch.empty((stats_len(E),), dtype=torch.float32, device=dev) if return_stats else None
     rt, _alive = _routing(T, top_k, dev, replay, replay_mask, dynamic_threshold, capacity_factor, seq_len, kept, stats)
-    args = (_ptr(x2), _ptr(router.contiguous()), _ptr(gate_up_proj.contiguous()), _ptr(down_proj.contiguous()),
+    # contiguous, 16-byte aligned operands, held until the call has been enqueued
+    x2, rt_w, gu, dn = (_aligned16(t) for t in (x2, router, gate_up_proj, down_proj))
+    if workspace.data_ptr() % 16:
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    args = (_ptr(x2), _ptr(rt_w), _ptr(gu), _ptr(dn),
             *(_ptr(b) for b in biases), _ptr(out), _ptr(sel), _ptr(w), _ptr(logits), _ptr(counts), _ptr(workspace),
             nbytes, stream)
     if rt is None:
@@ -348,7 +359,8 @@ def dispatch(x, router, *, top_k, norm_topk_prob=True, router_bias=None, num_exp
     stream = torch.cuda.current_stream(dev).cuda_stream
     kept = torch.empty((T, top_k), dtype=torch.uint8, device=dev)
     rt, _alive = _routing(T, top_k, dev, replay, replay_mask, dynamic_threshold, capacity_factor, seq_len, kept, None)
-    _check(moe_dispatch_routed(desc, rt, _ptr(x2), _ptr(router.contiguous()), _ptr(rb), _ptr(r["selected_experts"]),
+    router_c = router.contiguous()  # held until the call has been enqueued
+    _check(moe_dispatch_routed(desc, rt, _ptr(x2), _ptr(router_c), _ptr(rb), _ptr(r["selected_experts"]),
                                _ptr(r["routing_weights"]), _ptr(r["router_logits"]), _ptr(r["expert_counts"]),
                                _ptr(r["expert_offsets"]), _ptr(r["sorted_token"]), _ptr(r["sorted_slot"]),
                                _ptr(ws), nbytes, stream))

@@ -330,6 +330,8 @@ moe_status forward_impl(const moe_desc* d, const moe_routing* r, const void* x, 
   if (d->T == 0) return MOE_OK;
   if (!x || !router || !gate_up_proj || !down_proj || !out || !selected_experts || !routing_weights || !workspace)
     return MOE_EINVAL;
+  // the GEMMs' direct-to-LDS loads move 16-byte chunks
+  if (!aligned16(x) || !aligned16(gate_up_proj) || !aligned16(down_proj) || !aligned16(workspace)) return MOE_EINVAL;
   RoutePlan rp;
   st = plan_routing(d, r, &rp);
   if (st != MOE_OK) return st;

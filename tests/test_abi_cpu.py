@@ -124,6 +124,12 @@ def test_missing_pointers_and_small_workspace(lib):
                            None) == moe.MOE_EINVAL
     assert moe.moe_forward(d, fake, fake, fake, fake, None, None, None, fake, fake, fake, None, None, fake, need - 1,
                            None) == moe.MOE_EWORKSPACE
+    # x, gate_up_proj, down_proj and the workspace must start on 16-byte boundaries
+    odd = fake + 2
+    for i in (0, 2, 3, 12):
+        args = [fake, fake, fake, fake, None, None, None, fake, fake, fake, None, None, fake]
+        args[i] = odd
+        assert moe.moe_forward(d, *args, need, None) == moe.MOE_EINVAL, i
 
 
 def test_zero_tokens_is_a_no_op(lib):

@@ -332,6 +332,31 @@ def test_router_is_batch_invariant(E, K):
         np.testing.assert_array_equal(c[k], a[k][:T1])
 
 
+def test_misaligned_views_are_realigned():
+    """Views that start off a 16-byte boundary go through the binding (which
+    copies them) and give the aligned tensors' results bitwise."""
+    inp = workloads.generate(workloads.small_config(300, 128, 256, 4, 2, dtype="bf16", cfg_id=953))
+    d = device_inputs(inp)
+    c = inp["cfg"]
+
+    def off_by_one(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 16 != 0
+        return v
+
+    def run(x, gu, dn):
+        out, sel, w = moe.forward(x, d["router"], gu, dn, top_k=c["K"], router_bias=d["router_bias"])
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy(), sel.cpu().numpy(), w.cpu().numpy()
+
+    a = run(d["x"], d["gate_up"], d["down"])
+    b = run(off_by_one(d["x"]), off_by_one(d["gate_up"]), off_by_one(d["down"]))
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
 def test_timed_entry_point_matches_forward():
     """moe_forward_timed is moe_forward plus event records: bitwise equal outputs."""
     import ctypes
