@@ -1,12 +1,14 @@
-// bf16 grouped expert GEMM for gfx950: the prefill- and decode-sized
-// variants of the gate_up and down projections (epilogues in
-// gemm_epilogue.h; arithmetic as in grouped_gemm.hip: fp32 accumulation, one
-// rounding of h to bf16).
+// Grouped expert GEMM for gfx950 with direct-to-LDS operand loads, bf16 or
+// fp32: the prefill- and decode-sized variants of the gate_up and down
+// projections (epilogues in gemm_epilogue.h; arithmetic as in
+// grouped_gemm.hip: fp32 accumulation, one rounding of h to the compute
+// dtype).
 //
 // Tile: BM sorted rows x 256 weight rows (SwiGLU: 128 gate + the 128 matching
 // up rows, so 128 h columns; otherwise 256 output columns).  MFMA
-// v_mfma_f32_32x32x16_bf16 with the weights as operand 0, so a lane's
-// accumulators are groups of four consecutive output columns of one row.
+// v_mfma_f32_32x32x16_bf16 (fp32: four v_mfma_f32_32x32x2f32 per 16-byte
+// fragment) with the weights as operand 0, so a lane's accumulators are
+// groups of four consecutive output columns of one row.
 // The 256-row tile runs 8 waves (two per SIMD) as a 4 x 2 grid of 64 x 128
 // wave tiles and can take an expert's tail of up to kTailRows more rows; the
 // 128-row tile runs 4 waves (2 x 2); the decode tile (BM 32) runs 4 waves
@@ -27,9 +29,9 @@
 // stage S-1 steps before it is consumed with one barrier per step, waited on
 // only for the loads of the stage being published.
 //
-// Requires K % 64 == 0, 16-byte aligned operands, and operand regions under
-// 4 GiB (32-bit byte offsets); the host routes anything else to the generic
-// kernel.
+// Requires K to fill whole 128-byte stages (K % 64 == 0 for bf16, K % 32 == 0
+// for fp32), 16-byte aligned operands, and operand regions under 4 GiB
+// (32-bit byte offsets); the host routes anything else to the generic kernel.
 #include <type_traits>
 
 #include "gemm_epilogue.h"
@@ -42,6 +44,23 @@ namespace {
 // writes LDS bytes [dst + 16*l, dst + 16*l + 16); dst must be wave-uniform.
 __device__ __forceinline__ void lds_dma16(const char* src, char* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// One pair of 16-byte fragments into a 32x32 fp32 accumulator.  bf16: one
+// v_mfma_f32_32x32x16_bf16 (8 k per lane).  fp32: four v_mfma_f32_32x32x2f32
+// on the fragments' elements: lanes 0-31 and 32-63 hold 4 consecutive k of
+// two chunks, and MFMA i sums element i of both, so every k of the two chunks
+// enters once, in the same pairing for both operands.
+template <typename T>
+__device__ __forceinline__ f32x16 mfma_frag(const bf16x8& b, const bf16x8& a, f32x16 c) {
+  if constexpr (T::kBytes == 2) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
+  } else {
+    const f32x4 bv = __builtin_bit_cast(f32x4, b), av = __builtin_bit_cast(f32x4, a);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[i], av[i], c, 0, 0, 0);
+    return c;
+  }
 }
 
 // s_waitcnt vmcnt(N) with expcnt and lgkmcnt left unconstrained (gfx9
@@ -75,8 +94,10 @@ using ShapeM256 = Shape<256, 8, 4, 128, 2>;  // 2 x 68 KB of LDS (with the tail 
 using ShapeM128 = Shape<128, 4, 2, 128, 2>;  // 2 x 48 KB
 using ShapeM32 = Shape<32, 4, 1, 128, 4>;    // 4 x 36 KB
 
-template <int EPI, class SH>
+template <typename T, int EPI, class SH>
 __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
+  using elem = typename T::elem;
+  constexpr int EB = T::kBytes;
   constexpr int BM = SH::BM;
   constexpr bool DUAL = EPI == EPI_SWIGLU;
   constexpr int NW = SH::NW;
@@ -111,7 +132,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   if ((int)blockIdx.x >= a.num_work[0]) return;
   // K steps of KB/2 elements; a split item covers steps [kb0, ke0) of its
   // tile and leaves its fp32 partial sums for launch_split_fixup.
-  const int nk = (int)(a.Kd / (KB / 2));
+  const int nk = (int)(a.Kd / (KB / EB));
   constexpr bool SPLITTABLE = EPI != EPI_DOWN_ATOMIC && (BM == 256 || BM == 32);
   int2 wk = a.work[blockIdx.x];
   int kb0 = 0, ke0 = nk, split_slot = -1;
@@ -153,7 +174,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     const int rA = (w * AI + i) * RPI + lr;
     const int r = r0 + (rA < rows ? rA : 0);
     const int64_t src = a.a_index ? (int64_t)a.a_index[r] : (int64_t)r;
-    aoff[i] = (uint32_t)(src * a.lda * 2) + (uint32_t)(((lane % CPR) ^ swz(rA)) * 16);
+    aoff[i] = (uint32_t)(src * a.lda * EB) + (uint32_t)(((lane % CPR) ^ swz(rA)) * 16);
   }
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
@@ -166,7 +187,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
       const int64_t nn = n0 + rB;
       wr = nn < N ? nn : N - 1;
     }
-    boff[i] = (uint32_t)(wr * a.ldb * 2) + (uint32_t)(((lane % CPR) ^ swz(rB)) * 16);
+    boff[i] = (uint32_t)(wr * a.ldb * EB) + (uint32_t)(((lane % CPR) ^ swz(rB)) * 16);
   }
   // Tail rows BM .. BM+XRC-1: wave w loads rows BM + 8w .. BM + 8w + 7, of
   // strip w/4 (a wave whose strip is empty or absent loads nothing).
@@ -175,10 +196,10 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     const int rA = BM + w * RPI + lr;
     const int r = r0 + (rA < rows ? rA : 0);
     const int64_t src = a.a_index ? (int64_t)a.a_index[r] : (int64_t)r;
-    aoffx = (uint32_t)(src * a.lda * 2) + (uint32_t)(((lane % CPR) ^ swz(rA)) * 16);
+    aoffx = (uint32_t)(src * a.lda * EB) + (uint32_t)(((lane % CPR) ^ swz(rA)) * 16);
   }
   const char* Abase = static_cast<const char*>(a.A);
-  const char* Bbase = static_cast<const char*>(a.B) + (int64_t)e * a.b_estride * 2;
+  const char* Bbase = static_cast<const char*>(a.B) + (int64_t)e * a.b_estride * EB;
 
   // Loads of stage kt into its buffer.  The stepped schedule of the other
   // shapes issues past the end of the K range: the last stage is then
@@ -285,16 +306,15 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         for (int mi = 0; mi < SM; ++mi) {
 #pragma unroll
           for (int j = 0; j < NB; ++j)
-            acc[j / SN][mi][j % SN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[u][j], fa[u][mi],
-                                                                            acc[j / SN][mi][j % SN], 0, 0, 0);
+            acc[j / SN][mi][j % SN] = mfma_frag<T>(fb[u][j], fa[u][mi], acc[j / SN][mi][j % SN]);
           if constexpr (XT) {
             if (mi == 0) {
               const bf16x8 b0 = wg ? fb[u][J0 + DJ] : fb[u][J0];
-              accx[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, fx[u], accx[0], 0, 0, 0);
+              accx[0] = mfma_frag<T>(b0, fx[u], accx[0]);
             }
             if (mi == SM - 1) {
               const bf16x8 b1 = wg ? fb[u][J1 + DJ] : fb[u][J1];
-              accx[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, fx[u], accx[1], 0, 0, 0);
+              accx[1] = mfma_frag<T>(b1, fx[u], accx[1]);
             }
           }
         }
@@ -396,8 +416,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
           }
 #pragma unroll
           for (int j = 0; j < NB; ++j)
-            acc[j / SN][mi][j % SN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[t & 1][j], fa[g & 1],
-                                                                            acc[j / SN][mi][j % SN], 0, 0, 0);
+            acc[j / SN][mi][j % SN] = mfma_frag<T>(fb[t & 1][j], fa[g & 1], acc[j / SN][mi][j % SN]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -471,7 +490,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         const f32x16& c1 = acc[NACC - 1][mi][ni];
         const f32x4 v0{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
         const f32x4 v1{c1[4 * q4], c1[4 * q4 + 1], c1[4 * q4 + 2], c1[4 * q4 + 3]};
-        epilogue4<uint16_t, EPI>(a, rc, n0 + wn * WN + ni * 32 + 8 * q4 + 4 * h, v0, v1, bias);
+        epilogue4<elem, EPI>(a, rc, n0 + wn * WN + ni * 32 + 8 * q4 + 4 * h, v0, v1, bias);
       }
   }
   if constexpr (XRC > 0) {
@@ -486,7 +505,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
           const f32x16& c1 = accx[DUAL ? 1 : i];
           const f32x4 v0{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
           const f32x4 v1{c1[4 * q4], c1[4 * q4 + 1], c1[4 * q4 + 2], c1[4 * q4 + 3]};
-          epilogue4<uint16_t, EPI>(a, rc, n0 + xcol(i) + 8 * q4 + 4 * h, v0, v1, bias);
+          epilogue4<elem, EPI>(a, rc, n0 + xcol(i) + 8 * q4 + 4 * h, v0, v1, bias);
         }
     }
   }
@@ -499,7 +518,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 // gate and up sums; ReLU; the down projection's weighted slot store).
 constexpr int kFixupBlocksPerTile = 4;
 
-template <int EPI>
+template <typename T, int EPI>
 __global__ __launch_bounds__(256) void split_fixup_kernel(GemmArgs a) {
   const int R = a.split_info[0], P = a.split_info[1];
   const int j = blockIdx.x / kFixupBlocksPerTile;
@@ -537,39 +556,38 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmArgs a) {
       }
     }
     const RowCtx rc = row_ctx<EPI>(a, r0 + m);
-    epilogue4<uint16_t, EPI>(a, rc, n0 + c, s0, s1, bias);
+    epilogue4<typename T::elem, EPI>(a, rc, n0 + c, s0, s1, bias);
   }
 }
 
-template <int EPI>
+template <typename T, int EPI>
 hipError_t launch_rows(int var, const GemmArgs& a, hipStream_t s) {
   switch (var) {
     case VAR_BF16_M256:
-      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, ShapeM256>), dim3(a.max_work), dim3(ShapeM256::NW * 64), 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_kernel<T, EPI, ShapeM256>), dim3(a.max_work), dim3(ShapeM256::NW * 64), 0, s, a);
       break;
     case VAR_BF16_M128:
-      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, ShapeM128>), dim3(a.max_work), dim3(ShapeM128::NW * 64), 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_kernel<T, EPI, ShapeM128>), dim3(a.max_work), dim3(ShapeM128::NW * 64), 0, s, a);
       break;
     default:
-      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, ShapeM32>), dim3(a.max_work), dim3(ShapeM32::NW * 64), 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_kernel<T, EPI, ShapeM32>), dim3(a.max_work), dim3(ShapeM32::NW * 64), 0, s, a);
       break;
   }
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_split_fixup(int epi, const GemmArgs& a, int32_t ncu, hipStream_t s) {
-  if (ncu <= 0) return hipSuccess;
+template <typename T>
+hipError_t launch_fixup_tag(int epi, const GemmArgs& a, int32_t ncu, hipStream_t s) {
   switch (epi) {
     case EPI_SWIGLU:
-      hipLaunchKernelGGL(split_fixup_kernel<EPI_SWIGLU>, dim3(ncu * kFixupBlocksPerTile), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((split_fixup_kernel<T, EPI_SWIGLU>), dim3(ncu * kFixupBlocksPerTile), dim3(256), 0, s, a);
       break;
     case EPI_RELU:
-      hipLaunchKernelGGL(split_fixup_kernel<EPI_RELU>, dim3(ncu * kFixupBlocksPerTile), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((split_fixup_kernel<T, EPI_RELU>), dim3(ncu * kFixupBlocksPerTile), dim3(256), 0, s, a);
       break;
     case EPI_DOWN_SLOT:
-      hipLaunchKernelGGL(split_fixup_kernel<EPI_DOWN_SLOT>, dim3(ncu * kFixupBlocksPerTile), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((split_fixup_kernel<T, EPI_DOWN_SLOT>), dim3(ncu * kFixupBlocksPerTile), dim3(256), 0, s,
+                         a);
       break;
     default:
       return hipErrorInvalidValue;
@@ -577,13 +595,25 @@ hipError_t launch_split_fixup(int epi, const GemmArgs& a, int32_t ncu, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_bf16(int epi, int var, const GemmArgs& a, hipStream_t s) {
+template <typename T>
+hipError_t launch_gemm_tag(int epi, int var, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
-    case EPI_SWIGLU: return launch_rows<EPI_SWIGLU>(var, a, s);
-    case EPI_RELU: return launch_rows<EPI_RELU>(var, a, s);
-    case EPI_DOWN_ATOMIC: return launch_rows<EPI_DOWN_ATOMIC>(var, a, s);
-    default: return launch_rows<EPI_DOWN_SLOT>(var, a, s);
+    case EPI_SWIGLU: return launch_rows<T, EPI_SWIGLU>(var, a, s);
+    case EPI_RELU: return launch_rows<T, EPI_RELU>(var, a, s);
+    case EPI_DOWN_ATOMIC: return launch_rows<T, EPI_DOWN_ATOMIC>(var, a, s);
+    default: return launch_rows<T, EPI_DOWN_SLOT>(var, a, s);
   }
+}
+
+}  // namespace
+
+hipError_t launch_split_fixup(int dtype, int epi, const GemmArgs& a, int32_t ncu, hipStream_t s) {
+  if (ncu <= 0) return hipSuccess;
+  return dtype == 1 ? launch_fixup_tag<BF16>(epi, a, ncu, s) : launch_fixup_tag<F32>(epi, a, ncu, s);
+}
+
+hipError_t launch_gemm_bf16(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s) {
+  return dtype == 1 ? launch_gemm_tag<BF16>(epi, var, a, s) : launch_gemm_tag<F32>(epi, var, a, s);
 }
 
 }  // namespace moe

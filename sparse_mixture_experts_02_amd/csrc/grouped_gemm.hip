@@ -281,7 +281,7 @@ int variant_cols(int var, bool dual) {
 hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s) {
   if (a.max_work <= 0 || a.N <= 0) return hipSuccess;
   if (var == VAR_GENERIC_M64) return dtype == 1 ? launch_tag<BF16, 64>(epi, a, s) : launch_tag<F32, 64>(epi, a, s);
-  if (var != VAR_GENERIC) return launch_gemm_bf16(epi, var, a, s);
+  if (var != VAR_GENERIC) return launch_gemm_bf16(dtype, epi, var, a, s);
   return dtype == 1 ? launch_tag<BF16, 128>(epi, a, s) : launch_tag<F32, 128>(epi, a, s);
 }
 

@@ -59,15 +59,17 @@ moe_status check_desc(const moe_desc* d) {
   return MOE_OK;
 }
 
-// Variant for one GEMM: the bf16 direct-to-LDS kernel when K is a multiple of
-// 64 and byte offsets fit in 32 bits; its row tile follows the mean number of
-// rows per expert (decode-sized segments get 32-row tiles).
+// Variant for one GEMM: the direct-to-LDS kernel (bf16 or fp32) when K fills
+// whole 128-byte stages and byte offsets fit in 32 bits; its row tile follows
+// the mean number of rows per expert (decode-sized segments get 32-row tiles).
 GemmPlan plan_gemm(const moe_desc* d, int64_t M, int64_t N, int64_t Kd, int64_t a_rows, int64_t b_expert_elems,
                    bool dual) {
   GemmPlan p;
-  const bool bf16_ok = d->dtype == MOE_BF16 && Kd % 64 == 0 && a_rows * Kd * 2 < (int64_t)UINT32_MAX &&
-                       b_expert_elems * 2 < (int64_t)UINT32_MAX;
-  if (bf16_ok) {
+  // whole 128-byte K stages and 32-bit byte offsets
+  const int eb = elem_bytes(d->dtype);
+  const bool direct_ok = Kd % (128 / eb) == 0 && a_rows * Kd * eb < (int64_t)UINT32_MAX &&
+                         b_expert_elems * eb < (int64_t)UINT32_MAX;
+  if (direct_ok) {
     const int64_t mean = M / d->E;
     p.var = mean >= 512 ? VAR_BF16_M256 : (mean >= 64 ? VAR_BF16_M128 : VAR_BF16_M32);
   } else {
@@ -383,7 +385,7 @@ moe_status forward_impl(const moe_desc* d, const moe_routing* r, const void* x, 
   }
   const int epi1 = swiglu ? EPI_SWIGLU : EPI_RELU;
   if (launch_grouped_gemm(d->dtype, epi1, L.g1.var, g, s) != hipSuccess) return MOE_EDEVICE;
-  if (L.split1 && ncu > 0 && launch_split_fixup(epi1, g, ncu, s) != hipSuccess) return MOE_EDEVICE;
+  if (L.split1 && ncu > 0 && launch_split_fixup(d->dtype, epi1, g, ncu, s) != hipSuccess) return MOE_EDEVICE;
   if (!mk.mark(3)) return MOE_EDEVICE;
 
   GemmArgs h = g;
@@ -416,7 +418,7 @@ moe_status forward_impl(const moe_desc* d, const moe_routing* r, const void* x, 
   if (launch_grouped_gemm(d->dtype, d->deterministic ? EPI_DOWN_SLOT : EPI_DOWN_ATOMIC, L.g2.var, h, s) !=
       hipSuccess)
     return MOE_EDEVICE;
-  if (L.split2 && ncu > 0 && launch_split_fixup(EPI_DOWN_SLOT, h, ncu, s) != hipSuccess) return MOE_EDEVICE;
+  if (L.split2 && ncu > 0 && launch_split_fixup(d->dtype, EPI_DOWN_SLOT, h, ncu, s) != hipSuccess) return MOE_EDEVICE;
   if (!mk.mark(4)) return MOE_EDEVICE;
 
   if (d->deterministic || d->out_dtype == MOE_BF16) {

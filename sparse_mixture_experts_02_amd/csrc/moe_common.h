@@ -158,9 +158,10 @@ enum Epilogue { EPI_SWIGLU = 0, EPI_RELU = 1, EPI_DOWN_ATOMIC = 2, EPI_DOWN_SLOT
 //   GENERIC: any K / alignment, fp32 or bf16; 128x128 output tiles, operands
 //            staged through registers into LDS (GENERIC_M64: 64-row tiles,
 //            for GEMMs with too few 128-row items to fill two rounds).
-//   BF16_Mxxx: bf16 with K a multiple of 64 and 16-byte aligned rows; LDS
-//            double buffer filled by direct global->LDS loads; xxx rows per
-//            tile (256 and 128 for prefill, 32 for decode-sized segments).
+//   BF16_Mxxx: bf16 with K a multiple of 64, or fp32 with K a multiple of 32
+//            (whole 128-byte stages), 16-byte aligned rows; LDS stages filled
+//            by direct global->LDS loads; xxx rows per tile (256 and 128 for
+//            prefill, 32 for decode-sized segments).
 enum Variant { VAR_GENERIC = 0, VAR_BF16_M256 = 1, VAR_BF16_M128 = 2, VAR_BF16_M32 = 3, VAR_GENERIC_M64 = 4 };
 int variant_rows(int var);
 int variant_cols(int var, bool dual);
@@ -206,8 +207,9 @@ hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, h
 constexpr int kTailRows = 32;
 constexpr int32_t kTailTile = (int32_t)0x80000000;
 constexpr int kSplitTileRows = 256 + kTailRows, kSplitTileCols = 256;
-hipError_t launch_split_fixup(int epi, const GemmArgs& a, int32_t ncu, hipStream_t s);
-hipError_t launch_gemm_bf16(int epi, int var, const GemmArgs& a, hipStream_t s);
+hipError_t launch_split_fixup(int dtype, int epi, const GemmArgs& a, int32_t ncu, hipStream_t s);
+// The direct-to-LDS variants (VAR_BF16_*) for dtype 1 (bf16) or 0 (fp32).
+hipError_t launch_gemm_bf16(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s);
 
 struct FinalizeArgs {
   const float* src;   // slot rows (T*K, D) when K > 0 slots, or (T, D) accumulation
