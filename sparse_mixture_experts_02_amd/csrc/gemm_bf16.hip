@@ -516,7 +516,9 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 // and applies the tile's epilogue to the
 // sums, exactly as an unsplit tile applies it to its accumulators (SwiGLU:
 // gate and up sums; ReLU; the down projection's weighted slot store).
-constexpr int kFixupBlocksPerTile = 4;
+// 16 blocks of ~18 rows: each thread's chain of dependent loads stays short
+// (4 blocks per tile measured 7% slower on the fp32 ReLU layer).
+constexpr int kFixupBlocksPerTile = 16;
 
 template <typename T, int EPI>
 __global__ __launch_bounds__(256) void split_fixup_kernel(GemmArgs a) {

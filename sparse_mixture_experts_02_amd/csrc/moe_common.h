@@ -200,7 +200,7 @@ struct GemmArgs {
 hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s);
 // Sums the K parts of every split tile in part order and applies the tile's
 // epilogue `epi` (SwiGLU, ReLU or the down projection's slot store) to the
-// sums.  Four blocks per tile slot, `ncu` slots; blocks past R's exit.
+// sums.  Sixteen blocks per tile slot, `ncu` slots; blocks past R's exit.
 // A work item {expert | column_tile << 8, first_row | kTailTile} is the last
 // row tile of its expert and holds all of the expert's remaining rows (at most
 // BM + kTailRows; 256-row bf16 tiles only).
