@@ -201,8 +201,26 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DispatchArgs a) {
   const int cb = worker ? (int)((int64_t)j * nch / J) : 0;
   const int ce = worker ? (int)((int64_t)(j + 1) * nch / J) : 0;
 
+  // A worker's chunk counts (2 to kScanBatch of them) are loaded in one
+  // batch (addresses clamped into its range, the extra lanes masked) and
+  // kept for the bases below; single chunks and longer ranges loop.
+  constexpr int kScanBatch = 16;
+  const int per = ce - cb;
+  const bool batched = per > 1 && per <= kScanBatch;
+  int cc[kScanBatch];
   int s = 0;
-  for (int b = cb; b < ce; ++b) s += a.chunk_counts[(int64_t)b * E + e];
+  if (batched) {
+#pragma unroll
+    for (int q = 0; q < kScanBatch; ++q) {
+      const int b = min(cb + q, max(ce - 1, 0));
+      const int v = a.chunk_counts[(int64_t)b * E + e];
+      cc[q] = q < per ? v : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < kScanBatch; ++q) s += cc[q];
+  } else {
+    for (int b = cb; b < ce; ++b) s += a.chunk_counts[(int64_t)b * E + e];
+  }
   // Exclusive scan over j of part[j*E + e] for every expert at once: a
   // Hillis-Steele scan whose strides are multiples of E.
   const int n = J * E;
@@ -232,11 +250,20 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DispatchArgs a) {
   }
   if (worker) {
     int base = offs[e] + part[j * E + e];
-    for (int b = cb; b < ce; ++b) {
-      const int64_t idx = (int64_t)b * E + e;
-      const int c = a.chunk_counts[idx];
-      a.chunk_base[idx] = base;
-      base += c;
+    if (batched) {
+#pragma unroll
+      for (int q = 0; q < kScanBatch; ++q)
+        if (q < per) {
+          a.chunk_base[(int64_t)(cb + q) * E + e] = base;
+          base += cc[q];
+        }
+    } else {
+      for (int b = cb; b < ce; ++b) {
+        const int64_t idx = (int64_t)b * E + e;
+        const int c = a.chunk_counts[idx];
+        a.chunk_base[idx] = base;
+        base += c;
+      }
     }
   }
 
