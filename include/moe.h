@@ -17,8 +17,8 @@
  * "Compute the experts and router" and "Weight the selected outputs"), and the
  * Dew "Mixture of experts" page, section "Expert computation and placement"
  * (tokens are sorted into expert order and the experts run as one grouped
- * matrix product; each contraction accumulates in at least fp32 and rounds once
- * to the compute dtype).
+ * matrix product; a product's running sums are kept in fp32 or wider and its
+ * result is rounded to the working precision a single time).
  *
  * Conventions for every entry point
  *   - Tensors are contiguous, row-major DEVICE pointers unless stated.  Weights

@@ -20,7 +20,15 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
-_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+# MOE_ORACLE_LIB selects another build of the same source (the sanitizer
+# build of the test suite); it is loaded as it is, never rebuilt here.
+_LIB_ENV = os.environ.get("MOE_ORACLE_LIB")
+_LIB = _LIB_ENV or os.path.join(_HERE, "libmoe_oracle.so")
+
+# Flags of the AddressSanitizer + UndefinedBehaviorSanitizer build: any report
+# aborts the process (no recovery), frames are kept for the report.
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
 
 F32, BF16 = 0, 1
 SWIGLU, RELU = 0, 1
@@ -29,6 +37,8 @@ _lib = None
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if _LIB_ENV:
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off",
@@ -37,10 +47,18 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_sanitized(path: str) -> str:
+    """Compile the same source with AddressSanitizer and UBSan into ``path``
+    (host code only; load it with the ASan runtime preloaded)."""
+    subprocess.check_call(["gcc", *SANITIZE_FLAGS, "-std=c11", "-fno-fast-math", "-ffp-contract=off",
+                           "-shared", "-fPIC", "-pthread", _SRC, "-o", path, "-lm"])
+    return path
+
+
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not _LIB_ENV and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32

@@ -224,7 +224,7 @@ def make_desc(T, D, F, E, K, *, norm_topk_prob=True, act="silu", dtype=None, out
                    deterministic=int(bool(deterministic)))
 
 
-def _prepare(x, router, gate_up_proj, down_proj, top_k, act):
+def _prepare(x, router, gate_up_proj, down_proj, top_k, act, biases=(None, None, None)):
     torch = _torch()
     if x.dtype == torch.float64:
         raise TypeError("float64 input is not supported")
@@ -238,6 +238,7 @@ def _prepare(x, router, gate_up_proj, down_proj, top_k, act):
     G = 1 if act == "relu" else 2
     if gate_up_proj.shape != (E, G * F, D):
         raise ValueError("gate_up_proj must be %s, got %s" % ((E, G * F, D), tuple(gate_up_proj.shape)))
+    _check_biases(*biases, D, F, E, act)
     for t in (router, gate_up_proj, down_proj):
         if t.dtype != x.dtype:
             raise TypeError("x and the weights must share one dtype")
@@ -246,6 +247,17 @@ def _prepare(x, router, gate_up_proj, down_proj, top_k, act):
     if x.device.type != "cuda":
         raise ValueError("tensors must live on a ROCm device")
     return D, F, E
+
+
+def _check_biases(router_bias, up_bias, down_bias, D, F, E, act):
+    """The kernels read router_bias as (E), up_bias as (E, G*F) (the up half
+    at +F for SwiGLU) and down_bias as (E, D): any other shape is refused
+    before a pointer reaches them."""
+    G = 1 if act == "relu" else 2
+    for name, b, shape in (("router_bias", router_bias, (E,)), ("up_bias", up_bias, (E, G * F)),
+                           ("down_bias", down_bias, (E, D))):
+        if b is not None and tuple(b.shape) != shape:
+            raise ValueError("%s must be %s, got %s" % (name, shape, tuple(b.shape)))
 
 
 def _routing(T, top_k, dev, replay, replay_mask, dynamic_threshold, capacity_factor, seq_len, kept, stats):
@@ -285,7 +297,7 @@ def forward(x, router, gate_up_proj, down_proj, *, top_k, norm_topk_prob=True, a
     over sequences of ``seq_len`` tokens (default: all T).
     """
     torch = _torch()
-    D, F, E = _prepare(x, router, gate_up_proj, down_proj, top_k, act)
+    D, F, E = _prepare(x, router, gate_up_proj, down_proj, top_k, act, (router_bias, up_bias, down_bias))
     lead = x.shape[:-1]
     x2 = x.reshape(-1, D).contiguous()
     T = x2.shape[0]
@@ -355,6 +367,11 @@ def dispatch(x, router, *, top_k, norm_topk_prob=True, router_bias=None, num_exp
              sorted_token=torch.empty((M,), dtype=torch.int32, device=dev),
              sorted_slot=torch.empty((M,), dtype=torch.int32, device=dev))
     ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    if router.dim() != 2 or router.shape[1] != D or router.shape[0] != E:
+        raise ValueError("router must be (E, D) = (%d, %d), got %s" % (E, D, tuple(router.shape)))
+    _check_biases(router_bias, None, None, D, F, E, "silu")
+    if router.dtype != x.dtype:
+        raise TypeError("x and the router must share one dtype")
     rb = None if router_bias is None else router_bias.to(device=dev, dtype=torch.float32).contiguous()
     stream = torch.cuda.current_stream(dev).cuda_stream
     kept = torch.empty((T, top_k), dtype=torch.uint8, device=dev)

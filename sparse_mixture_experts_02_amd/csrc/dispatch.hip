@@ -63,35 +63,11 @@ __device__ int block_exclusive_scan(int* v, int* tmp, int n) {
   return total;
 }
 
-// Position of work item b in the operand-sharing order.  Blocks are handed
-// to the 8 XCDs round-robin (b % 8).  Contiguous: XCD x receives one
-// contiguous range of the order.  Windows: an XCD's 32 CUs run its blocks in
-// rounds of 32, so the order is dealt out in windows of 32 items, XCD x
-// taking windows x, x + 8, x + 16, ...; its 32 concurrently running tiles are
-// then one window of the order (with 8 row tiles per expert, exactly one
-// group of 4 column tiles x 8 row tiles) and share 4 weight column tiles and
-// 8 row tiles of activations in its L2, where contiguous ranges straddle the
-// groups (prefill layer -2..-3.4%; the decode weight stream is 3% slower
-// with windows).  Items past the last whole 256-item round go to the XCDs
-// in contiguous ranges.  A bijection of [0, total).
-__device__ __forceinline__ int xcd_order(int b, int total, bool windows) {
-  const int full = windows ? (total / 256) * 256 : 0;
-  if (b < full) {
-    const int i = b / 8, x = b % 8;
-    return 256 * (i / 32) + 32 * x + i % 32;
-  }
-  b -= full;
-  total -= full;
-  const int q = total / 8, r = total % 8, x = b % 8, i = b / 8;
-  return full + (x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i);
-}
-
 // Work lists of the grouped GEMMs from the per-expert counts `cnts` and
-// segment offsets `offs` (both in LDS).  Order: experts ascending; inside an
-// expert, groups of kColGroup column tiles; inside a group, column tile
-// slowest and row tile fastest.  Empty experts contribute no item.  Called by
-// all kScanThreads threads of one block; `tst` (E+1) and `tmp`
-// (kScanThreads) are LDS scratch.
+// segment offsets `offs` (both in LDS), by the rules of worklist.h (tile
+// counts, the tail decision, the item order, the XCD order, the K split).
+// Empty experts contribute no item.  Called by all kScanThreads threads of
+// one block; `tst` (E+1) and `tmp` (kScanThreads) are LDS scratch.
 __device__ void build_work_lists(const DispatchArgs& a, const int* cnts, const int* offs, int* tst, int* tmp) {
   const int tid = threadIdx.x;
   const int E = a.E;
@@ -105,68 +81,24 @@ __device__ void build_work_lists(const DispatchArgs& a, const int* cnts, const i
     // (a K-split part's share when that round is split, else a whole tile).
     bool tails = false;
     if (sp.xr > 0 && sp.ncu > 0) {
-      if (tid < E) tst[tid] = (cnts[tid] + sp.bm - 1) / sp.bm;
+      if (tid < E) tst[tid] = row_tiles(cnts[tid], sp.bm, 0);
       __syncthreads();
       const int plain = block_exclusive_scan(tst, tmp, E) * sp.ntn;
-      if (tid < E) {
-        const int c = cnts[tid];
-        tst[tid] = c == 0 ? 0 : max(1, (c - sp.xr + sp.bm - 1) / sp.bm);
-      }
+      if (tid < E) tst[tid] = row_tiles(cnts[tid], sp.bm, sp.xr);
       __syncthreads();
       const int fused = block_exclusive_scan(tst, tmp, E) * sp.ntn;
-      auto rounds = [&](int total) {
-        const int R = total % sp.ncu;
-        int P = 1;
-        if (sp.split_ncu > 0 && R > 0) P = min(kMaxSplitParts, sp.split_ncu / R);
-        return (float)(total / sp.ncu) + (R == 0 ? 0.f : (P >= 2 ? 1.f / P : 1.f));
-      };
-      tails = rounds(fused) < rounds(plain);
+      tails = est_rounds(fused, sp.ncu, sp.split_ncu) < est_rounds(plain, sp.ncu, sp.split_ncu);
     }
-    const int xr = tails ? sp.xr : 0;
-    if (tid < E) {
-      const int c = cnts[tid];
-      tst[tid] = c == 0 ? 0 : max(1, (c - xr + sp.bm - 1) / sp.bm);
-    }
+    if (tid < E) tst[tid] = row_tiles(cnts[tid], sp.bm, tails ? sp.xr : 0);
     __syncthreads();
     const int tiles = block_exclusive_scan(tst, tmp, E);
     if (tid == 0) tst[E] = tiles;
     __syncthreads();
     const int ntn = sp.ntn;
     const int total = tiles * ntn;
-    // The item at position L of the order.
-    auto item = [&](int L) {
-      // expert: the last x with tst[x] * ntn <= L
-      int lo = 0, hi = E;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (tst[mid] * ntn <= L) lo = mid; else hi = mid;
-      }
-      const int x = lo;
-      const int mt = tst[x + 1] - tst[x];
-      const int q = L - tst[x] * ntn;
-      const int full = (ntn / kColGroup) * kColGroup * mt;
-      int m, n;
-      if (q < full) {
-        const int gsz = kColGroup * mt;
-        const int grp = q / gsz, r = q - grp * gsz;
-        n = grp * kColGroup + r / mt;
-        m = r % mt;
-      } else {
-        const int r = q - full;
-        n = (ntn / kColGroup) * kColGroup + r / mt;
-        m = r % mt;
-      }
-      // the last tile of an expert with more than bm remaining rows holds them all
-      const bool tail = m == mt - 1 && offs[x + 1] - (offs[x] + m * sp.bm) > sp.bm;
-      return make_int2(x | (n << 8), (offs[x] + m * sp.bm) | (tail ? kTailTile : 0));
-    };
     // Items past the last full round of split_ncu blocks are cut along K.
-    int R = 0, P = 1;
-    if (sp.split_ncu > 0 && total > 0) {
-      R = total % sp.split_ncu;
-      P = R > 0 ? min(kMaxSplitParts, sp.split_ncu / R) : 1;
-      if (P < 2) R = 0, P = 1;
-    }
+    int R, P;
+    split_plan(total, sp.split_ncu, &R, &P);
     const int F = total - R;
     const int n_items = F + R * P;
     if (tid == 0) {
@@ -176,12 +108,13 @@ __device__ void build_work_lists(const DispatchArgs& a, const int* cnts, const i
         sp.split_info[1] = P;
       }
     }
-    for (int j = tid; j < R; j += kScanThreads) sp.split_tiles[j] = item(F + j);
+    for (int j = tid; j < R; j += kScanThreads) sp.split_tiles[j] = work_item(F + j, tst, offs, E, ntn, sp.bm);
     // Blocks [0, F) take the full items in the XCD order; blocks [F, F+R*P)
     // the split parts, which blocks b % 8 spread evenly over the XCDs and
     // which dispatch last.
     for (int b = tid; b < n_items && b < sp.max_work; b += kScanThreads)
-      sp.work[b] = b < F ? item(xcd_order(b, F, sp.windows != 0)) : make_int2(kSplitItem | (b - F), 0);
+      sp.work[b] = b < F ? work_item(xcd_order(b, F, sp.windows != 0), tst, offs, E, ntn, sp.bm)
+                         : make_int2(kSplitItem | (b - F), 0);
   }
 }
 
@@ -243,10 +176,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DispatchArgs a) {
   }
   __syncthreads();
   const int M = block_exclusive_scan(offs, tmp, E);
+  // Thread E writes the end offset from its own copy of the total: offs[E]
+  // is written by thread 0, which for E >= 64 sits in another wave, and is
+  // read by other threads only after the next barrier.
   if (tid == 0) offs[E] = M;
   if (tid <= E) {
-    a.offsets[tid] = offs[tid];
-    if (a.offsets_out) a.offsets_out[tid] = offs[tid];
+    const int o = tid == E ? M : offs[tid];
+    a.offsets[tid] = o;
+    if (a.offsets_out) a.offsets_out[tid] = o;
   }
   if (worker) {
     int base = offs[e] + part[j * E + e];
@@ -365,10 +302,11 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_small_kernel(DispatchAr
   }
   __syncthreads();
   const int M = block_exclusive_scan(offs, tmp, E);
-  if (tid == 0) offs[E] = M;
+  if (tid == 0) offs[E] = M;  // read by other threads after the barrier below
   if (tid <= E) {
-    a.offsets[tid] = offs[tid];
-    if (a.offsets_out) a.offsets_out[tid] = offs[tid];
+    const int o = tid == E ? M : offs[tid];
+    a.offsets[tid] = o;
+    if (a.offsets_out) a.offsets_out[tid] = o;
   }
   __syncthreads();
   if (valid) {

@@ -137,23 +137,21 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   int2 wk = a.work[blockIdx.x];
   int kb0 = 0, ke0 = nk, split_slot = -1;
   if constexpr (SPLITTABLE) {
-    if (wk.x < 0) {
-      const int q = wk.x & 0x7fffffff;
+    if (item_is_split(wk)) {
       const int P = a.split_info[1];
-      const int j = q / P, p = q - j * P;
+      int j, p;
+      split_part(wk, P, &j, &p);
       wk = a.split_tiles[j];
-      kb0 = p * nk / P;
-      ke0 = (p + 1) * nk / P;
-      split_slot = q;
+      split_k_range(p, P, nk, &kb0, &ke0);
+      split_slot = j * P + p;
     }
   }
-  const int e = wk.x & 0xff;
-  const int r0 = wk.y & 0x7fffffff;
+  const int e = item_expert(wk);
+  const int r0 = item_first_row(wk);
   // A tile flagged kTailTile holds all of its expert's remaining rows (at
   // most BM + XRC by construction of the work lists; clamped all the same).
-  const int rem = a.offsets[e + 1] - r0;
-  const int rows = min(rem, (wk.y & kTailTile) ? BM + XRC : BM);
-  const int64_t n0 = (int64_t)(wk.x >> 8) * OUTC;
+  const int rows = item_rows(a.offsets[e + 1] - r0, item_is_tail(wk), BM, XRC);
+  const int64_t n0 = (int64_t)item_col_tile(wk) * OUTC;
   const int64_t N = a.N;
 
   const int lane = threadIdx.x & 63;
@@ -529,14 +527,14 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmArgs a) {
   constexpr bool DUAL = EPI == EPI_SWIGLU;
   constexpr int OUTC = DUAL ? kSplitTileCols / 2 : kSplitTileCols;
   const int2 wk = a.split_tiles[j];
-  const int e = wk.x & 0xff;
-  const int r0 = wk.y & 0x7fffffff;
-  const int rem = a.offsets[e + 1] - r0;
-  const int rows = min(rem, (wk.y & kTailTile) ? a.split_bm + kTailRows : a.split_bm);  // as the GEMM's tiles
+  const int e = item_expert(wk);
+  const int r0 = item_first_row(wk);
+  // as the GEMM's tiles
+  const int rows = item_rows(a.offsets[e + 1] - r0, item_is_tail(wk), a.split_bm, kTailRows);
   // this block's share of the tile's rows
   const int rs = (rows + kFixupBlocksPerTile - 1) / kFixupBlocksPerTile;
   const int m0 = sub * rs, m1 = min(rows, m0 + rs);
-  const int64_t n0 = (int64_t)(wk.x >> 8) * OUTC;
+  const int64_t n0 = (int64_t)item_col_tile(wk) * OUTC;
   const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;
   constexpr int C4 = OUTC / 4;
   for (int idx = m0 * C4 + (int)threadIdx.x; idx < m1 * C4; idx += 256) {

@@ -77,10 +77,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 
   if ((int)blockIdx.x >= a.num_work[0]) return;
   const int2 wk = a.work[blockIdx.x];
-  const int e = wk.x & 0xff;
-  const int r0 = wk.y;
-  const int rows = min(BM, a.offsets[e + 1] - r0);
-  const int64_t n0 = (int64_t)(wk.x >> 8) * BN;
+  const int e = item_expert(wk);
+  const int r0 = item_first_row(wk);  // the generic lists have neither tails nor splits
+  const int rows = item_rows(a.offsets[e + 1] - r0, false, BM, 0);
+  const int64_t n0 = (int64_t)item_col_tile(wk) * BN;
   const int64_t N = a.N, Kd = a.Kd;
   const bool vec = a.vec_ok != 0;
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "worklist.h"
+
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -128,9 +130,6 @@ struct WorkSpec {
   // stream, and the generic kernel).
   int32_t windows;
 };
-constexpr int kColGroup = 4;  // column tiles per ordering group
-constexpr int kMaxSplitParts = 8;  // K parts per split item at most (4 measured 0.5-4% slower with the 16-block fix-up)
-constexpr int32_t kSplitItem = (int32_t)0x80000000;
 
 struct DispatchArgs {
   const int32_t* sel32;   // (M) expert of assignment i = t*K + k; E = dropped
@@ -201,11 +200,6 @@ hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, h
 // Sums the K parts of every split tile in part order and applies the tile's
 // epilogue `epi` (SwiGLU, ReLU or the down projection's slot store) to the
 // sums.  Sixteen blocks per tile slot, `ncu` slots; blocks past R's exit.
-// A work item {expert | column_tile << 8, first_row | kTailTile} is the last
-// row tile of its expert and holds all of the expert's remaining rows (at most
-// BM + kTailRows; 256-row bf16 tiles only).
-constexpr int kTailRows = 32;
-constexpr int32_t kTailTile = (int32_t)0x80000000;
 constexpr int kSplitTileRows = 256 + kTailRows, kSplitTileCols = 256;
 hipError_t launch_split_fixup(int dtype, int epi, const GemmArgs& a, int32_t ncu, hipStream_t s);
 // The direct-to-LDS variants (VAR_BF16_*) for dtype 1 (bf16) or 0 (fp32).

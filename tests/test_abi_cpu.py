@@ -178,3 +178,28 @@ def test_probes_validate_on_the_host(lib):
     assert moe.moe_probe_read(4104, 1024, 4, 4096, None) == einval   # buffer not 16-byte aligned
     assert moe.moe_probe_read(4096, 1024, 0, 4096, None) == einval
 
+
+
+@pytest.mark.parametrize("act,which,shape", [
+    ("silu", "router_bias", (9,)), ("silu", "router_bias", (8, 1)),
+    ("silu", "up_bias", (8, 128)),          # an (E, F) bias on a SwiGLU layer: the up half would be read past it
+    ("silu", "up_bias", (256,)),            # one bias shared by the experts
+    ("relu", "up_bias", (8, 256)),
+    ("silu", "down_bias", (8, 128)), ("relu", "down_bias", (64,)),
+])
+def test_bias_shapes_are_checked_before_any_pointer_is_passed(act, which, shape):
+    """The kernels index the router bias as (E), the up bias as (E, G*F) and
+    the down bias as (E, D): the binding refuses anything else with a
+    ValueError naming the bias (on CPU tensors the check comes before the
+    device check, so no GPU is needed)."""
+    torch = pytest.importorskip("torch")
+    E, D, F = 8, 64, 128
+    G = 1 if act == "relu" else 2
+    x = torch.zeros(5, D)
+    args = (x, torch.zeros(E, D), torch.zeros(E, G * F, D), torch.zeros(E, D, F))
+    good = dict(router_bias=torch.zeros(E), up_bias=torch.zeros(E, G * F), down_bias=torch.zeros(E, D))
+    with pytest.raises(ValueError, match="ROCm device"):
+        moe.forward(*args, top_k=2, act=act, **good)
+    bad = dict(good, **{which: torch.zeros(*shape)})
+    with pytest.raises(ValueError, match=which):
+        moe.forward(*args, top_k=2, act=act, **bad)

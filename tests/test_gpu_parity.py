@@ -4,7 +4,9 @@ Every call goes through the C ABI (ctypes binding over libmoe.so).  Sizes:
 the small workloads are compared token by token in full; the full-size
 workloads (the Mixtral-shaped prefill and decode, the 128-expert layer) run
 at their real shape in the configuration the benchmark times and are compared
-on sampled tokens, plus properties that hold for every token.
+on the tokens of the first and last row of every 64-row strip of every expert
+segment (every row tile, tail tile and K-split tile of both GEMMs), plus
+properties that hold for every token.
 """
 import os
 
@@ -12,7 +14,8 @@ import numpy as np
 import pytest
 
 import workloads
-from parity import check, check_full_properties, device_inputs, gpu_forward, to_device
+from parity import (assert_strata_covered, check, check_full_properties, device_inputs, gpu_forward,
+                    stratified_tokens, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,10 +32,29 @@ def _say(msg):
     print("[gpu-parity] " + msg, flush=True)
 
 
-def _sample(T, n, seed=0):
-    rng = np.random.default_rng(seed)
-    s = rng.choice(T, size=min(n, T), replace=False)
-    return np.unique(np.concatenate([s, [0, T - 1]]))
+STRIP = 64  # every row tile of the 256- and 128-row GEMM tiles starts at a multiple of 64 in its segment
+
+
+def _strata(inp, g, d=None):
+    """Compared tokens: the first and last row of every 64-row strip of every
+    expert segment of the sorted order (so every row tile of both GEMMs, each
+    tail tile and each K-split tile has compared rows), plus tokens 0 and T-1.
+    With the device inputs at hand the order is taken from moe.dispatch and
+    checked bit-exact against a stable argsort of the layer's selection."""
+    c = inp["cfg"]
+    T, E, K = c["T"], c["E"], c["K"]
+    tok, rows, offs, order = stratified_tokens(g["sel"], E, STRIP)
+    if d is not None:
+        r = moe.dispatch(d["x"], d["router"], top_k=K, norm_topk_prob=c["norm"], router_bias=d["router_bias"])
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(r["selected_experts"].cpu().numpy(), g["sel"])
+        np.testing.assert_array_equal(r["expert_offsets"].cpu().numpy(), offs)
+        np.testing.assert_array_equal(r["sorted_slot"].cpu().numpy(), order)
+        np.testing.assert_array_equal(r["sorted_token"].cpu().numpy(), order // K)
+    tok = np.unique(np.concatenate([tok, [0, T - 1]]))
+    assert_strata_covered(tok, g["sel"], E, STRIP)
+    _say("compared tokens %d (rows %d of %d)" % (tok.size, rows.size, T * K))
+    return tok
 
 
 # ------------------------------------------------------------ small, full
@@ -104,6 +126,14 @@ EDGE = [
     (70000, 64, 64, 8, 2, "swiglu", "f32", False, True),
     (150, 320, 64, 130, 3, "swiglu", "bf16", False, True),
 ]
+# The highest-index expert carries most rows (its segment ends at offsets[E]),
+# over 64 or more experts, on the one-block and the multi-block sort.
+EDGE_LAST = [
+    (100, 128, 192, 128, 8, "swiglu", "bf16", False, True),
+    (3000, 128, 256, 128, 8, "swiglu", "bf16", False, True),
+    (2500, 64, 96, 256, 4, "relu", "f32", True, True),
+    (700, 256, 320, 65, 2, "swiglu", "bf16", False, True),
+]
 
 
 @pytest.mark.parametrize("case", EDGE, ids=lambda c: "T%d_D%d_F%d_E%d_K%d_%s_%s_b%d_n%d" % tuple(c))
@@ -115,6 +145,20 @@ def test_edge_shapes(case, det):
     inp = workloads.generate(cfg)
     _say("edge %s det=%s" % (case, det))
     g = gpu_forward(inp, deterministic=det)
+    check(inp, g)
+    check_full_properties(inp, g)
+
+
+@pytest.mark.parametrize("case", EDGE_LAST, ids=lambda c: "T%d_D%d_F%d_E%d_K%d_%s_%s_b%d_n%d" % tuple(c))
+@pytest.mark.parametrize("det", [False, True])
+def test_edge_last_expert_heavy(case, det):
+    T, D, F, E, K, act, dt, biases, norm = case
+    cfg = workloads.small_config(T, D, F, E, K, act=act, dtype=dt, norm=norm, biases=biases,
+                                 router_bias="last_heavy", cfg_id=260 + E + K)
+    inp = workloads.generate(cfg)
+    _say("edge-last %s det=%s" % (case, det))
+    g = gpu_forward(inp, deterministic=det)
+    assert g["counts"][E - 1] > T // 2
     check(inp, g)
     check_full_properties(inp, g)
 
@@ -203,6 +247,33 @@ def test_dispatch_is_a_stable_counting_sort(T):
     assert np.array_equal(sel, gpu_forward(inp, d)["sel"])
 
 
+@pytest.mark.parametrize("E,T,K", [(64, 100, 4), (65, 100, 4), (128, 100, 8), (256, 250, 4),   # one-block sort
+                                   (64, 3000, 4), (128, 3000, 8), (256, 5000, 4)])            # multi-block sort
+def test_dispatch_many_experts_last_expert_loaded(E, T, K):
+    """Routers with 64 or more experts, the highest-index expert favoured by a
+    router bias so that it holds many rows: the end offset (written by thread
+    E of the scan block, in another wave than thread 0) must be T*K exactly,
+    and the order a stable argsort, on both the one-block (T*K <= 1024) and
+    the multi-block sort."""
+    cfg = workloads.small_config(T, 64, 64, E, K, dtype="bf16", router_bias="last_heavy", cfg_id=405)
+    inp = workloads.generate(cfg)
+    d = device_inputs(inp)
+    _say("dispatch E=%d T=%d K=%d" % (E, T, K))
+    r = moe.dispatch(d["x"], d["router"], top_k=K, router_bias=d["router_bias"])
+    torch.cuda.synchronize()
+    sel = r["selected_experts"].cpu().numpy()
+    counts = r["expert_counts"].cpu().numpy()
+    offs = r["expert_offsets"].cpu().numpy()
+    flat = sel.ravel()
+    assert counts[E - 1] == T, "the favoured expert should take every token"
+    assert offs[E] == T * K
+    assert np.array_equal(counts, np.bincount(flat, minlength=E))
+    assert np.array_equal(offs, np.concatenate([[0], np.cumsum(counts)]))
+    order = np.argsort(flat, kind="stable")
+    assert np.array_equal(r["sorted_slot"].cpu().numpy(), order)
+    assert np.array_equal(r["sorted_token"].cpu().numpy(), order // K)
+
+
 # ----------------------------------------------------- full-size workloads
 _CACHE = {}
 
@@ -224,13 +295,13 @@ def _prefill_family():
 
 
 @pytest.mark.slow
-def test_prefill_mixtral_shape_sampled():
+def test_prefill_mixtral_shape_stratified():
     inp = _prefill_family()
     d = device_inputs(inp)
     _say("prefill T=8192 D=4096 F=14336 E=8 K=2 bf16")
     g = gpu_forward(inp, d)
     check_full_properties(inp, g)
-    st = check(inp, g, tokens=_sample(8192, 48))
+    st = check(inp, g, tokens=_strata(inp, g, d))
     _say(str(st))
     _CACHE["prefill_dev"] = d
     _CACHE["prefill_gpu"] = g
@@ -268,19 +339,19 @@ def test_one_expert_share_full_size():
     g = gpu_forward(inp, deterministic=True)
     check_full_properties(inp, g)
     assert np.all(g["weights"] == 1.0) and np.all(g["sel"] == 0)
-    st = check(inp, g, tokens=_sample(2080, 24, seed=3))
+    st = check(inp, g, tokens=_strata(inp, g))
     _say(str(st))
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["fine", "fine_zero"])
-def test_fine_grained_128_experts_sampled(name):
+def test_fine_grained_128_experts_stratified(name):
     inp = _inputs(name)
     d = device_inputs(inp)
     _say("%s T=16384 D=2048 F=768 E=128 K=8 bf16" % name)
     g = gpu_forward(inp, d, deterministic=name == "fine_zero")
     check_full_properties(inp, g)
-    st = check(inp, g, tokens=_sample(16384, 96, seed=1))
+    st = check(inp, g, tokens=_strata(inp, g, d))
     _say(str(st))
     if name == "fine_zero":
         z = workloads.zero_load_experts(128)

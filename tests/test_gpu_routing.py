@@ -19,7 +19,8 @@ import pytest
 
 import oracle
 import workloads
-from parity import BF16_TOL, F32_TOL, NEAR_TIE, W_TOL, device_inputs, to_device
+from parity import (BF16_TOL, F32_TOL, NEAR_TIE, W_TOL, assert_strata_covered, device_inputs, stratified_tokens,
+                    to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -134,6 +135,17 @@ def compare_stats(inp, gpu, ref):
     np.testing.assert_allclose(s[2 * E:3 * E], r["frac_routed"], rtol=1e-6, atol=1e-7)
     for i, k in enumerate(("switch", "gshard", "master", "gshard_probs")):
         assert abs(s[3 * E + i] - r[k]) <= STATS_TOL * max(abs(r[k]), 1e-3), (k, s[3 * E + i], r[k])
+
+
+def strata(sel, kept, E, strip=64):
+    """Tokens of the first and last row of every `strip`-row strip of every
+    expert segment of the kept assignments' sorted order (every row tile of
+    both GEMMs has compared rows), plus tokens 0 and T-1."""
+    T = sel.shape[0]
+    tok = np.unique(np.concatenate([stratified_tokens(sel, E, strip, kept)[0], [0, T - 1]]))
+    assert_strata_covered(tok, sel, E, strip, kept)
+    _say("compared tokens %d" % tok.size)
+    return tok
 
 
 def _cfg(T, D, F, E, K, dtype="f32", **kw):
@@ -317,16 +329,16 @@ def test_stats_are_reproducible():
 
 # ------------------------------------------------------ full-size workloads
 @pytest.mark.slow
-def test_prefill_capacity_full_size_sampled():
+def test_prefill_capacity_full_size_stratified():
     """The Mixtral-shaped prefill (T=8192) as two 4096-token sequences at
-    capacity factor 1.0, compared on sampled tokens; kept flags and counts
-    for every token."""
+    capacity factor 1.0, compared on the tokens of every 64-row strip's first
+    and last row of every expert segment; kept flags and counts for every
+    token."""
     inp = workloads.generate("prefill")
     T = inp["cfg"]["T"]
-    rng = np.random.default_rng(3)
-    tok = np.unique(np.concatenate([rng.choice(T, 40, replace=False), [0, T - 1]]))
     _say("prefill capacity T=%d" % T)
     g = run_gpu(inp, capacity_factor=1.0, seq_len=4096)
+    tok = strata(g["sel"], g["kept"], inp["cfg"]["E"])
     ref, ex = reference(inp, g, tokens=tok, capacity_factor=1.0, seq_len=4096)
     st = compare(inp, g, ref, tokens=tok)
     compare_stats(inp, g, ref)
@@ -334,18 +346,18 @@ def test_prefill_capacity_full_size_sampled():
 
 
 @pytest.mark.slow
-def test_fine_experts_threshold_and_capacity_full_size_sampled():
+def test_fine_experts_threshold_and_capacity_full_size_stratified():
     """The 128-expert workload (T=16384, K=8, Zipf-skewed loads) with a
     dynamic threshold and capacity factor 1.25 over four 4096-token
     sequences: kept flags, counts and statistics for every token, outputs on
-    sampled tokens."""
+    the tokens of every 64-row strip's first and last row of every expert
+    segment."""
     inp = workloads.generate("fine")
     T = inp["cfg"]["T"]
     thr = safe_threshold(inp, 0.3)
-    rng = np.random.default_rng(4)
-    tok = np.unique(np.concatenate([rng.choice(T, 24, replace=False), [0, T - 1]]))
-    _say("fine threshold %.6f + capacity 1.25 x 4096" % thr)
+    _say("fine threshold %.6f + capacity 1.25 x 4096, T=%d" % (thr, T))
     g = run_gpu(inp, dynamic_threshold=thr, capacity_factor=1.25, seq_len=4096)
+    tok = strata(g["sel"], g["kept"], inp["cfg"]["E"])
     ref, ex = reference(inp, g, tokens=tok, threshold=thr, capacity_factor=1.25, seq_len=4096)
     st = compare(inp, g, ref, tokens=tok)
     compare_stats(inp, g, ref)
@@ -353,7 +365,7 @@ def test_fine_experts_threshold_and_capacity_full_size_sampled():
 
 
 @pytest.mark.slow
-def test_prefill_replay_full_size_sampled():
+def test_prefill_replay_full_size_stratified():
     """The Mixtral-shaped prefill replaying a record that differs from the own
     selection (each covered token's experts shifted by one) on 60% of the
     tokens."""
@@ -363,10 +375,9 @@ def test_prefill_replay_full_size_sampled():
     own = oracle.route(inp["x"], inp["router"], top_k=K)["sel"]
     record = (own + 1) % E
     mask = np.random.default_rng(6).random(T) < 0.6
-    rng = np.random.default_rng(7)
-    tok = np.unique(np.concatenate([rng.choice(T, 40, replace=False), [0, T - 1]]))
     _say("prefill replay T=%d covered=%d" % (T, mask.sum()))
     g = run_gpu(inp, replay=record, replay_mask=mask)
+    tok = strata(g["sel"], g["kept"], E)
     ref, ex = reference(inp, g, tokens=tok, replay=record, replay_mask=mask)
     st = compare(inp, g, ref, tokens=tok)
     np.testing.assert_array_equal(g["sel"][mask], record[mask])
@@ -393,9 +404,9 @@ def test_tail_rows_join_last_tile(act, D, F, deterministic):
     record = np.stack([labels[:T], labels[T:]], axis=1)
     assert np.all(record[:, 0] != record[:, 1])
     inp = _cfg(T, D, F, E, K, dtype="bf16", act=act, cfg_id=270 + D % 7)
-    tokens = None if D <= 256 else np.sort(np.random.default_rng(5).choice(T, 96, replace=False))
     _say("tail rows act=%s D=%d F=%d deterministic=%s counts=%s" % (act, D, F, deterministic, counts))
     g = run_gpu(inp, replay=record, deterministic=deterministic)
+    tokens = None if D <= 256 else strata(g["sel"], g["kept"], E, strip=32)
     np.testing.assert_array_equal(g["counts"], counts)
     ref, _ = reference(inp, g, tokens=tokens, replay=record)
     st = compare(inp, g, ref, tokens=tokens)

@@ -169,6 +169,11 @@ def generate(name_or_cfg, *, T: int | None = None, with_weights: bool = True) ->
         rb = zipf_rank_bias(E)
         if cfg["router_bias"] == "zipf_zero":
             rb[zero_load_experts(E)] -= np.float32(30.0)
+    elif cfg.get("router_bias") == "last_heavy":
+        # the highest-index expert is favoured: it takes most of the rows,
+        # the other experts share the rest
+        rb = np.zeros(E, dtype=np.float32)
+        rb[E - 1] = np.float32(2.0)
     out["router_bias"] = rb
     return out
 
