@@ -439,7 +439,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     if (split_slot >= 0) {
       // raw fp32 partial sums of this K range, tile-local rows x 256 columns
       // (SwiGLU: the gate sums in columns [0,128), the up sums in [128,256))
-      float* dst = a.partial + (int64_t)split_slot * (kSplitTileRows * kSplitTileCols);
+      float* dst = a.partial + (int64_t)split_slot * a.split_rows * kSplitTileCols;
 #pragma unroll
       for (int mi = 0; mi < SM; ++mi) {
         const int m = wm * WM + mi * 32 + l32;
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmArgs a) {
     const int m = idx / C4, c = (idx - m * C4) * 4;
     f32x4 s0{0.f, 0.f, 0.f, 0.f}, s1{0.f, 0.f, 0.f, 0.f};
     for (int p = 0; p < P; ++p) {
-      const float* src = a.partial + ((int64_t)(j * P + p) * kSplitTileRows + m) * kSplitTileCols + c;
+      const float* src = a.partial + ((int64_t)(j * P + p) * a.split_rows + m) * kSplitTileCols + c;
       const float4 v = *reinterpret_cast<const float4*>(src);
       s0[0] += v.x;
       s0[1] += v.y;

@@ -139,8 +139,10 @@ Layout layout_of(const moe_desc* d) {
     L.split_tiles2 = take(sizeof(int2) * kSplitMaxCU);
     L.split_info2 = take(sizeof(int32_t) * 2);
   }
-  if (L.split1 || L.split2)  // shared: the two GEMMs and their fix-ups run in order
-    L.partial = take(sizeof(float) * (size_t)kSplitMaxCU * kSplitTileRows * kSplitTileCols);
+  if (L.split1 || L.split2) {  // shared: the two GEMMs and their fix-ups run in order
+    const int32_t rows1 = L.split1 ? L.g1.bm + L.g1.xr : 0, rows2 = L.split2 ? L.g2.bm + L.g2.xr : 0;
+    L.partial = take(sizeof(float) * (size_t)kSplitMaxCU * (rows1 > rows2 ? rows1 : rows2) * kSplitTileCols);
+  }
   if (!d->deterministic && d->out_dtype == MOE_BF16) L.acc = take(sizeof(float) * T * D);
   L.total = off;
   return L;
@@ -382,6 +384,7 @@ moe_status forward_impl(const moe_desc* d, const moe_routing* r, const void* x, 
     g.split_info = at<int32_t>(workspace, L.split_info1);
     g.partial = at<float>(workspace, L.partial);
     g.split_bm = L.g1.bm;
+    g.split_rows = L.g1.bm + L.g1.xr;
   }
   const int epi1 = swiglu ? EPI_SWIGLU : EPI_RELU;
   if (launch_grouped_gemm(d->dtype, epi1, L.g1.var, g, s) != hipSuccess) return MOE_EDEVICE;
@@ -414,6 +417,7 @@ moe_status forward_impl(const moe_desc* d, const moe_routing* r, const void* x, 
     h.split_info = at<int32_t>(workspace, L.split_info2);
     h.partial = at<float>(workspace, L.partial);
     h.split_bm = L.g2.bm;
+    h.split_rows = L.g2.bm + L.g2.xr;
   }
   if (launch_grouped_gemm(d->dtype, d->deterministic ? EPI_DOWN_SLOT : EPI_DOWN_ATOMIC, L.g2.var, h, s) !=
       hipSuccess)

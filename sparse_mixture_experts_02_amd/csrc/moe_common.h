@@ -189,18 +189,19 @@ struct GemmArgs {
   int32_t vec_ok;           // rows 16-byte aligned: vector loads allowed
   // K-split items (256- and 32-row bf16 tiles, any epilogue but the atomic
   // combine): the partial sums of part p of split tile j go to partial +
-  // (j*P + p) tiles of kSplitTileRows x kSplitTileCols fp32, reduced by
+  // (j*P + p) tiles of split_rows x kSplitTileCols fp32, reduced by
   // launch_split_fixup.
   const int2* split_tiles;
   const int32_t* split_info;
   float* partial;
   int32_t split_bm;         // rows per split tile (the kernel variant's tile height)
+  int32_t split_rows;       // rows per partial tile in `partial`: split_bm plus the tail rows it may hold
 };
 hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s);
 // Sums the K parts of every split tile in part order and applies the tile's
 // epilogue `epi` (SwiGLU, ReLU or the down projection's slot store) to the
 // sums.  Sixteen blocks per tile slot, `ncu` slots; blocks past R's exit.
-constexpr int kSplitTileRows = 256 + kTailRows, kSplitTileCols = 256;
+constexpr int kSplitTileCols = 256;  // columns of a partial tile (rows: GemmArgs::split_rows)
 hipError_t launch_split_fixup(int dtype, int epi, const GemmArgs& a, int32_t ncu, hipStream_t s);
 // The direct-to-LDS variants (VAR_BF16_*) for dtype 1 (bf16) or 0 (fp32).
 hipError_t launch_gemm_bf16(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s);

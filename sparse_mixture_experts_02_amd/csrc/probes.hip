@@ -14,7 +14,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "moe.h"
+#include "moe_probes.h"
 
 namespace {
 

@@ -1,6 +1,7 @@
 """The C ABI without a GPU: the library loads, exports every entry point the
 header declares, and rejects bad arguments on the host before any launch."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -10,13 +11,15 @@ import pytest
 import sparse_mixture_experts_02_amd as moe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", src, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", src, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -29,8 +32,11 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("moe_forward", "moe_forward_timed", "moe_forward_routed", "moe_dispatch", "moe_dispatch_routed",
-              "moe_workspace_bytes", "moe_status_string", "moe_abi_version"):
+              "moe_workspace_bytes", "moe_status_string", "moe_abi_version", "moe_probe_mfma", "moe_probe_read"):
         assert n in names
+    # the layer's header carries the layer only; the probes have their own
+    layer = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "moe.h")).read(), flags=re.S)
+    assert "moe_probe" not in layer
 
 
 def test_every_declared_symbol_is_exported(lib):
