@@ -114,6 +114,27 @@ moe_status moe_forward(const moe_desc* d, const void* x, const void* router, con
                        void* stream);
 
 /*
+ * moe_forward_noalloc -- moe_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments and results without the workspace.
+ * The scratch memory is a fixed array of MOE_NOALLOC_MAX_BYTES in the
+ * library's device code, one per device, held from the first call on a
+ * device until the process ends; nothing is allocated per call.  A call whose
+ * moe_workspace_bytes exceeds MOE_NOALLOC_MAX_BYTES returns MOE_EWORKSPACE
+ * before any launch.  All calls on one device share that device's array:
+ * calls that may overlap on one device (other streams, other host threads)
+ * race and must be ordered by the caller.  Runs the kernels of moe_forward,
+ * so its outputs are bitwise those of moe_forward with deterministic = 1
+ * (and of the same atomic adds with 0).  MOE_EDEVICE if the array's device
+ * address cannot be obtained.
+ */
+#define MOE_NOALLOC_MAX_BYTES (64u << 20)
+moe_status moe_forward_noalloc(const moe_desc* d, const void* x, const void* router, const void* gate_up_proj,
+                               const void* down_proj, const float* router_bias, const float* up_bias,
+                               const float* down_bias, void* out, int64_t* selected_experts,
+                               float* routing_weights, float* router_logits, int32_t* expert_counts, void* stream);
+
+/*
  * moe_forward_timed -- moe_forward that also records caller-created HIP events
  * (hipEvent_t handles passed as void*) on `stream` at its stage boundaries, so
  * a caller can time each stage with hipEventElapsedTime.  events[0] is

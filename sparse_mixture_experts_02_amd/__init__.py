@@ -81,6 +81,8 @@ def load_library():
         lib.moe_workspace_bytes.restype = ctypes.c_int
         lib.moe_forward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
         lib.moe_forward.restype = ctypes.c_int
+        lib.moe_forward_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.moe_forward_noalloc.restype = ctypes.c_int
         lib.moe_forward_timed.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P, P, I32]
         lib.moe_forward_timed.restype = ctypes.c_int
         lib.moe_dispatch.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
@@ -140,6 +142,17 @@ def moe_forward(desc, x, router, gate_up_proj, down_proj, router_bias, up_bias, 
     return load_library().moe_forward(ctypes.byref(desc), x, router, gate_up_proj, down_proj, router_bias, up_bias,
                                       down_bias, out, selected_experts, routing_weights, router_logits,
                                       expert_counts, workspace, workspace_bytes, stream)
+
+
+MOE_NOALLOC_MAX_BYTES = 64 << 20
+
+
+def moe_forward_noalloc(desc, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out,
+                        selected_experts, routing_weights, router_logits, expert_counts, stream) -> int:
+    """Raw call of moe_forward_noalloc (no workspace argument); returns the status code."""
+    return load_library().moe_forward_noalloc(ctypes.byref(desc), x, router, gate_up_proj, down_proj, router_bias,
+                                              up_bias, down_bias, out, selected_experts, routing_weights,
+                                              router_logits, expert_counts, stream)
 
 
 def moe_forward_timed(desc, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out,
@@ -387,6 +400,7 @@ def dispatch(x, router, *, top_k, norm_topk_prob=True, router_bias=None, num_exp
 
 MOE_STAGE_EVENTS = 6
 
-__all__ = ["MoeDesc", "MoeRouting", "MoEError", "load_library", "moe_forward", "moe_forward_timed",
+__all__ = ["MoeDesc", "MoeRouting", "MoEError", "load_library", "moe_forward", "moe_forward_noalloc",
+           "moe_forward_timed",
            "moe_forward_routed", "moe_dispatch", "moe_dispatch_routed", "moe_workspace_bytes", "moe_status_string",
            "moe_abi_version", "make_desc", "stats_len", "forward", "dispatch", "LIB_PATH"]

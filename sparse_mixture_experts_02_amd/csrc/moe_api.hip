@@ -8,7 +8,15 @@
 #include <limits.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "moe_common.h"
+
+// Workspace of moe_forward_noalloc: one copy per device, held from the first
+// call on that device until the process ends.  Host code never passes this
+// name to a kernel (on the host it is only a stand-in for the symbol); it
+// uses the device address that hipGetSymbolAddress returns for it.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_MAX_BYTES];
 
 namespace {
 
@@ -465,6 +473,23 @@ moe_status dispatch_impl(const moe_desc* d, const moe_routing* r, const void* x,
                         static_cast<hipStream_t>(stream), none, false);
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+constexpr int kMaxDevices = 64;
+void* scratch_address() {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -509,6 +534,24 @@ moe_status moe_forward_routed(const moe_desc* d, const moe_routing* r, const voi
   return forward_impl(d, r, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out,
                       selected_experts, routing_weights, router_logits, expert_counts, workspace, workspace_bytes,
                       stream, nullptr, 0);
+}
+
+moe_status moe_forward_noalloc(const moe_desc* d, const void* x, const void* router, const void* gate_up_proj,
+                               const void* down_proj, const float* router_bias, const float* up_bias,
+                               const float* down_bias, void* out, int64_t* selected_experts,
+                               float* routing_weights, float* router_logits, int32_t* expert_counts, void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (layout_of(d).total > (size_t)MOE_NOALLOC_MAX_BYTES) return MOE_EWORKSPACE;
+  void* ws = scratch_address();
+  if (!ws) return MOE_EDEVICE;
+  // Every workspace section the layer reads is written earlier in the same
+  // call (nothing has to start at zero), so the previous call's contents do
+  // no harm.
+  return forward_impl(d, nullptr, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out,
+                      selected_experts, routing_weights, router_logits, expert_counts, ws,
+                      (size_t)MOE_NOALLOC_MAX_BYTES, stream, nullptr, 0);
 }
 
 moe_status moe_forward_timed(const moe_desc* d, const void* x, const void* router, const void* gate_up_proj,

@@ -209,3 +209,16 @@ def test_bias_shapes_are_checked_before_any_pointer_is_passed(act, which, shape)
     bad = dict(good, **{which: torch.zeros(*shape)})
     with pytest.raises(ValueError, match=which):
         moe.forward(*args, top_k=2, act=act, **bad)
+
+
+def test_noalloc_refuses_oversize_before_any_launch(lib):
+    # workspace of the Mixtral-shaped prefill (~0.75 GB) is above the fixed array
+    d = _desc(T=8192, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=1)
+    assert moe.moe_workspace_bytes(d) > moe.MOE_NOALLOC_MAX_BYTES
+    fake = 256
+    assert moe.moe_forward_noalloc(d, fake, fake, fake, fake, None, None, None, fake, fake, fake, None, None,
+                                   None) == moe.MOE_EWORKSPACE
+    # argument errors come first, as for moe_forward
+    assert moe.moe_forward_noalloc(_desc(K=0), fake, fake, fake, fake, None, None, None, fake, fake, fake, None,
+                                   None, None) == moe.MOE_EINVAL
+    assert moe.moe_forward_noalloc(_desc(T=0), *([None] * 12), None) == moe.MOE_OK

@@ -1,0 +1,98 @@
+"""moe_forward_noalloc through the C ABI (needs an MI355X).
+
+The entry point for callers that cannot allocate runs the layer on the
+library's fixed per-device scratch array.  Two calls in a row, the second
+with a smaller input (so it runs on the array the first call left behind),
+must give bitwise the outputs of moe_forward on a freshly allocated
+workspace; the first is also checked against the oracle.  A call whose
+workspace would exceed the array is refused before any launch.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from parity import check, device_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no ROCm device", allow_module_level=True)
+
+import sparse_mixture_experts_02_amd as moe  # noqa: E402
+
+
+def _say(msg):
+    print("[no-alloc] " + msg, flush=True)
+
+
+def _run(inp, d, noalloc):
+    c = inp["cfg"]
+    T, D, F, E, K = c["T"], c["D"], c["F"], c["E"], c["K"]
+    dt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
+    act = "silu" if c["act"] == "swiglu" else "relu"
+    desc = moe.make_desc(T, D, F, E, K, norm_topk_prob=c["norm"], act=act, dtype=dt, deterministic=True)
+    out = torch.full((T, D), float("nan"), dtype=torch.float32, device="cuda")
+    sel = torch.full((T, K), -1, dtype=torch.int64, device="cuda")
+    w = torch.full((T, K), float("nan"), dtype=torch.float32, device="cuda")
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    counts = torch.empty((E,), dtype=torch.int32, device="cuda")
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    common = [ptr(d["x"]), ptr(d["router"]), ptr(d["gate_up"]), ptr(d["down"]), ptr(d["router_bias"]),
+              ptr(d["up_bias"]), ptr(d["down_bias"]), ptr(out), ptr(sel), ptr(w), ptr(logits), ptr(counts)]
+    stream = torch.cuda.current_stream().cuda_stream
+    if noalloc:
+        assert moe.moe_workspace_bytes(desc) <= moe.MOE_NOALLOC_MAX_BYTES
+        st = moe.moe_forward_noalloc(desc, *common, stream)
+    else:
+        nbytes = moe.moe_workspace_bytes(desc)
+        ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
+        st = moe.moe_forward(desc, *common, ws.data_ptr(), nbytes, stream)
+    assert st == moe.MOE_OK, moe.moe_status_string(st)
+    torch.cuda.synchronize()
+    return dict(out=out.cpu().numpy(), sel=sel.cpu().numpy(), weights=w.cpu().numpy(), logits=logits.cpu().numpy(),
+                counts=counts.cpu().numpy())
+
+
+CALLS = [
+    # (T, D, F, E, K, act, dtype, biases): the second call is smaller than the first
+    (1000, 256, 512, 8, 2, "swiglu", "bf16", False),   # 128-row tiles
+    (40, 256, 384, 8, 2, "swiglu", "bf16", False),     # 32-row tiles with K-split parts
+]
+
+
+def test_noalloc_matches_forward_two_calls_second_smaller():
+    for i, (T, D, F, E, K, act, dt, biases) in enumerate(CALLS):
+        cfg = workloads.small_config(T, D, F, E, K, act=act, dtype=dt, biases=biases, router_bias="zipf",
+                                     cfg_id=970 + i)
+        inp = workloads.generate(cfg)
+        d = device_inputs(inp)
+        _say("call %d: T=%d D=%d F=%d E=%d K=%d %s %s" % (i, T, D, F, E, K, act, dt))
+        a = _run(inp, d, noalloc=True)
+        b = _run(inp, d, noalloc=False)
+        for k in ("out", "sel", "weights", "logits", "counts"):
+            np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+        if i == 0:
+            _say(str(check(inp, a)))
+
+
+def test_noalloc_fp32_relu_with_biases_after_a_larger_call():
+    # after the calls above (or alone): fp32 ReLU with all three biases
+    cfg = workloads.small_config(300, 96, 160, 6, 2, act="relu", dtype="f32", biases=True, cfg_id=975)
+    inp = workloads.generate(cfg)
+    d = device_inputs(inp)
+    a = _run(inp, d, noalloc=True)
+    b = _run(inp, d, noalloc=False)
+    for k in ("out", "sel", "weights", "logits", "counts"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    check(inp, a)
+
+
+def test_noalloc_refuses_more_than_its_array():
+    # Mixtral-shaped prefill: ~0.75 GB of workspace, far above the array.
+    desc = moe.make_desc(8192, 4096, 14336, 8, 2, dtype=torch.bfloat16, deterministic=True)
+    assert moe.moe_workspace_bytes(desc) > moe.MOE_NOALLOC_MAX_BYTES
+    fake = 256  # never dereferenced: the size check comes before any launch
+    st = moe.moe_forward_noalloc(desc, fake, fake, fake, fake, None, None, None, fake, fake, fake, None, None,
+                                 torch.cuda.current_stream().cuda_stream)
+    assert st == moe.MOE_EWORKSPACE
