@@ -113,9 +113,15 @@ Layout layout_of(const moe_desc* d) {
   // blocks (decode: 8 experts x 16 down column tiles is half a round).  The
   // down projection splits only in deterministic mode (the atomic combine
   // would add more than two terms per output).
-  auto splits = [](int var) { return var == VAR_BF16_M256 || var == VAR_BF16_M32; };
-  L.split1 = splits(L.g1.var);
-  L.split2 = d->deterministic && splits(L.g2.var);
+  // A split needs enough K steps to give every part some (8 parts at most):
+  // with fewer, the fix-up launch costs more than the shorter round saves
+  // (the tiny fp32 block has 2 K steps per GEMM).
+  const int eb = elem_bytes(d->dtype);
+  auto splits = [&](int var, int64_t Kd) {
+    return (var == VAR_BF16_M256 || var == VAR_BF16_M32) && Kd * eb / 128 >= kMaxSplitParts;
+  };
+  L.split1 = splits(L.g1.var, D);
+  L.split2 = d->deterministic && splits(L.g2.var, F);
   if (L.split1) L.g1.max_work += kSplitMaxCU;
   if (L.split2) L.g2.max_work += kSplitMaxCU;
   size_t off = 0;

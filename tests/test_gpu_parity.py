@@ -301,8 +301,16 @@ def test_prefill_mixtral_shape_stratified():
     _say("prefill T=8192 D=4096 F=14336 E=8 K=2 bf16")
     g = gpu_forward(inp, d)
     check_full_properties(inp, g)
-    st = check(inp, g, tokens=_strata(inp, g, d))
+    tok = _strata(inp, g, d)
+    st = check(inp, g, tokens=tok)
     _say(str(st))
+    # the same layer with the atomic combine (K = 2: reproducible) and with a
+    # bf16 output, on the same compared tokens
+    ga = gpu_forward(inp, d, deterministic=False)
+    np.testing.assert_array_equal(ga["sel"], g["sel"])
+    _say("atomic combine " + str(check(inp, ga, tokens=tok)))
+    gb = gpu_forward(inp, d, out_dtype=torch.bfloat16)
+    _say("bf16 output " + str(check(inp, gb, tokens=tok, out_bf16=True)))
     _CACHE["prefill_dev"] = d
     _CACHE["prefill_gpu"] = g
 
@@ -318,6 +326,22 @@ def test_decode_mixtral_shape_full():
     check_full_properties(inp, g)
     st = check(inp, g)
     _say(str(st))
+    # the entry point for callers that cannot allocate holds this shape in
+    # its fixed scratch array and gives bitwise the same results
+    c = inp["cfg"]
+    desc = moe.make_desc(64, c["D"], c["F"], c["E"], c["K"], dtype=torch.bfloat16, deterministic=True)
+    assert moe.moe_workspace_bytes(desc) <= moe.MOE_NOALLOC_MAX_BYTES
+    out = torch.empty((64, c["D"]), dtype=torch.float32, device="cuda")
+    sel = torch.empty((64, c["K"]), dtype=torch.int64, device="cuda")
+    w = torch.empty((64, c["K"]), dtype=torch.float32, device="cuda")
+    st = moe.moe_forward_noalloc(desc, dd["x"].data_ptr(), dd["router"].data_ptr(), dd["gate_up"].data_ptr(),
+                                 dd["down"].data_ptr(), None, None, None, out.data_ptr(), sel.data_ptr(),
+                                 w.data_ptr(), None, None, torch.cuda.current_stream().cuda_stream)
+    assert st == moe.MOE_OK
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), g["out"])
+    np.testing.assert_array_equal(sel.cpu().numpy(), g["sel"])
+    np.testing.assert_array_equal(w.cpu().numpy(), g["weights"])
     # the decode batch is the first 64 prefill tokens: same routing and output
     if "prefill_gpu" in _CACHE:
         pg = _CACHE["prefill_gpu"]
