@@ -67,12 +67,60 @@ def bf16_half_ulp(v):
     return np.where(a > 0, np.exp2(e - 8.0), 0.0)
 
 
+# Oracle results keyed by the inputs' sha256 manifest (workloads.input_sha256)
+# and the evaluated tokens: a workload compared several times (combine modes,
+# output dtypes) runs the oracle once.  MOE_ORACLE_CACHE_DIR adds a disk copy
+# (.npz) that later processes reuse.
+_ORACLE_CACHE = {}
+_SHA_OF = {}  # id()s of an input's arrays -> (the arrays, kept alive, and their sha256)
+_INPUT_KEYS = ("x", "router", "gate_up", "down", "router_bias", "up_bias", "down_bias")
+
+
+def _input_sha256(inp: dict) -> str:
+    import workloads
+    arrs = tuple(inp.get(k) for k in _INPUT_KEYS)
+    ids = tuple(id(a) for a in arrs)
+    hit = _SHA_OF.get(ids)
+    if hit is None:
+        hit = (arrs, workloads.input_sha256(inp))
+        if len(_SHA_OF) >= 8:  # keep a few inputs alive, not every one seen
+            _SHA_OF.pop(next(iter(_SHA_OF)))
+        _SHA_OF[ids] = hit
+    return hit[1]
+
+
+def oracle_reference(inp: dict, tokens) -> dict:
+    import hashlib
+    import os
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+    c = inp["cfg"]
+    key_src = "%s|%s|%s" % (_input_sha256(inp), hashlib.sha256(tokens.tobytes()).hexdigest(),
+                            (c["K"], c["norm"], c["act"]))
+    key = hashlib.sha256(key_src.encode()).hexdigest()
+    if key in _ORACLE_CACHE:
+        return {k: v.copy() for k, v in _ORACLE_CACHE[key].items()}
+    cdir = os.environ.get("MOE_ORACLE_CACHE_DIR")
+    path = os.path.join(cdir, "oracle_%s.npz" % key) if cdir else None
+    if path and os.path.exists(path):
+        with np.load(path) as z:
+            ref = {k: z[k] for k in z.files}
+    else:
+        ref = oracle.forward_inputs(inp, tokens=tokens)
+        ref = {k: v for k, v in ref.items() if isinstance(v, np.ndarray)}
+        if path:
+            os.makedirs(cdir, exist_ok=True)
+            np.savez(path + ".tmp.npz", **ref)
+            os.replace(path + ".tmp.npz", path)
+    _ORACLE_CACHE[key] = ref
+    return {k: v.copy() for k, v in ref.items()}
+
+
 def check(inp: dict, gpu: dict, tokens=None, *, out_bf16=False, max_exempt_frac=0.02) -> dict:
     """Compare GPU results (all tokens) with the oracle on ``tokens`` (default all)."""
     c = inp["cfg"]
     T = c["T"]
     tokens = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
-    ref = oracle.forward_inputs(inp, tokens=tokens)
+    ref = oracle_reference(inp, tokens)
     gsel = gpu["sel"][tokens]
     K = c["K"]
 

@@ -394,3 +394,25 @@ def test_fine_zero_experts_get_no_tokens():
     z = workloads.zero_load_experts(128)
     assert len(set(z.tolist())) == 8
     assert inp["x"].dtype == np.uint16
+
+
+def test_oracle_cache_returns_the_same_reference(tmp_path, monkeypatch):
+    """The parity helpers' oracle cache (keyed by the inputs' sha256 manifest
+    and the tokens) returns what a fresh oracle call returns, from memory and
+    from its disk copy, and a different input gets a different entry."""
+    import parity
+    monkeypatch.setenv("MOE_ORACLE_CACHE_DIR", str(tmp_path))
+    inp = workloads.generate(workloads.small_config(40, 16, 24, 4, 2, cfg_id=990))
+    tok = np.arange(0, 40, 3)
+    fresh = oracle.forward_inputs(inp, tokens=tok)
+    a = parity.oracle_reference(inp, tok)
+    assert len(list(tmp_path.glob("oracle_*.npz"))) == 1
+    parity._ORACLE_CACHE.clear()
+    b = parity.oracle_reference(dict(inp), tok)  # from disk
+    for k in ("out", "sel", "weights", "logits", "probs"):
+        np.testing.assert_array_equal(a[k], fresh[k])
+        np.testing.assert_array_equal(b[k], fresh[k])
+    other = dict(inp, x=inp["x"] + np.float32(1.0))
+    c = parity.oracle_reference(other, tok)
+    assert not np.array_equal(c["out"], a["out"])
+    assert len(list(tmp_path.glob("oracle_*.npz"))) == 2
