@@ -1,0 +1,112 @@
+"""The layer captured in a HIP graph (needs an MI355X).
+
+The library enqueues only kernels on the caller's stream (no memset, no
+allocation, no host synchronisation), so a caller can capture a whole layer
+call in a HIP graph and replay it.  Each test captures the call once, then
+replays the graph several times with the program's own eager work and
+synchronisations between the replays (new inputs copied into the captured
+buffers, other layer calls on the same stream), and checks every replay
+bitwise against an eager call on the same inputs.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from parity import check, device_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no ROCm device", allow_module_level=True)
+
+import sparse_mixture_experts_02_amd as moe  # noqa: E402
+
+
+def _say(msg):
+    print("[gpu-graph] " + msg, flush=True)
+
+
+class Call:
+    """Buffers and raw arguments of one layer call (moe_forward, or
+    moe_forward_noalloc when noalloc)."""
+
+    def __init__(self, inp, d, noalloc=False):
+        c = inp["cfg"]
+        self.T, self.D, self.E, self.K = c["T"], c["D"], c["E"], c["K"]
+        dt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
+        self.desc = moe.make_desc(c["T"], c["D"], c["F"], c["E"], c["K"], norm_topk_prob=c["norm"],
+                                  act="silu" if c["act"] == "swiglu" else "relu", dtype=dt, deterministic=True)
+        self.noalloc = noalloc
+        self.nbytes = moe.moe_workspace_bytes(self.desc)
+        self.ws = None if noalloc else torch.empty((self.nbytes,), dtype=torch.uint8, device="cuda")
+        self.x = d["x"].reshape(self.T, self.D).clone()
+        self.d = d
+        self.out = torch.empty((self.T, self.D), dtype=torch.float32, device="cuda")
+        self.sel = torch.empty((self.T, self.K), dtype=torch.int64, device="cuda")
+        self.w = torch.empty((self.T, self.K), dtype=torch.float32, device="cuda")
+        self.counts = torch.empty((self.E,), dtype=torch.int32, device="cuda")
+        self.logits = torch.empty((self.T, self.E), dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+        d = self.d
+        args = [p(self.x), p(d["router"]), p(d["gate_up"]), p(d["down"]), p(d["router_bias"]), p(d["up_bias"]),
+                p(d["down_bias"]), p(self.out), p(self.sel), p(self.w), p(self.logits), p(self.counts)]
+        stream = torch.cuda.current_stream().cuda_stream
+        if self.noalloc:
+            st = moe.moe_forward_noalloc(self.desc, *args, stream)
+        else:
+            st = moe.moe_forward(self.desc, *args, p(self.ws), self.nbytes, stream)
+        assert st == moe.MOE_OK, moe.moe_status_string(st)
+
+    def result(self):
+        return [t.cpu().numpy().copy() for t in (self.out, self.sel, self.w, self.logits, self.counts)]
+
+
+def _replay_matches_eager(inp, noalloc, n_replays=4):
+    d = device_inputs(inp)
+    call = Call(inp, d, noalloc=noalloc)
+    call()  # eager once before capture (also looks up the scratch array's address)
+    torch.cuda.synchronize()
+    out, sel, w, logits, counts = call.result()
+    check(inp, dict(out=out, sel=sel, weights=w, logits=logits, counts=counts))
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    x0 = call.x.clone()
+    other = Call(inp, d, noalloc=noalloc)  # eager work on the same stream between replays
+    for r in range(n_replays):
+        # new tokens: a row permutation and a scaling of the original batch
+        perm = torch.from_numpy(rng.permutation(call.T)).cuda()
+        scale = float(rng.uniform(0.5, 1.5))
+        newx = (x0[perm].float() * scale).to(x0.dtype)
+        call.x.copy_(newx)
+        g.replay()
+        torch.cuda.synchronize()
+        got = call.result()
+        other.x.copy_(newx)
+        other()
+        torch.cuda.synchronize()
+        want = other.result()
+        for a, b, name in zip(got, want, ("out", "sel", "weights", "logits", "counts")):
+            np.testing.assert_array_equal(a, b, err_msg="replay %d: %s" % (r, name))
+        _say("replay %d matches the eager call (noalloc=%s)" % (r, noalloc))
+    return g
+
+
+@pytest.mark.parametrize("noalloc", [False, True])
+@pytest.mark.parametrize("name_or_cfg", ["tiny", "relu_small", "bf16_small"])
+def test_graph_replay_matches_eager(name_or_cfg, noalloc):
+    if name_or_cfg == "relu_small":
+        name_or_cfg = workloads.small_config(700, 256, 512, 8, 2, act="relu", dtype="f32", biases=True, cfg_id=980)
+    elif name_or_cfg == "bf16_small":
+        name_or_cfg = workloads.small_config(1000, 512, 768, 16, 4, dtype="bf16", router_bias="zipf", cfg_id=981)
+    inp = workloads.generate(name_or_cfg)
+    _say("graph %s noalloc=%s" % (inp["cfg"].get("desc", inp["cfg"]), noalloc))
+    _replay_matches_eager(inp, noalloc)
