@@ -33,6 +33,23 @@ moe_status moe_probe_mfma(int32_t blocks, int32_t iters, float* out, void* strea
 int64_t moe_probe_mfma_flops(int32_t blocks, int32_t iters);
 moe_status moe_probe_read(const void* buf, int64_t bytes, int32_t blocks, float* out, void* stream);
 
+/*
+ * moe_gemm_plan: host-only (no device call) description of the two grouped
+ *   GEMMs a layer call with descriptor `d` runs: the gate_up GEMM (entries
+ *   0..5) and the down GEMM (6..11) of the host array `plan` (12 int32, owned
+ *   by the caller).  Per GEMM: kernel variant, rows per row tile, output
+ *   columns per column tile, column tiles, whether the last partial round of
+ *   work items may be split along K (0/1), and the work-list capacity.
+ *   Variants: 0 generic 128-row tiles; 1 direct-to-LDS 256-row tiles with
+ *   32-row tail strips; 2 direct-to-LDS 128-row tiles; 3 direct-to-LDS 32-row
+ *   tiles; 4 generic 64-row tiles; 5 weight-streaming 32-row tiles (bf16,
+ *   contraction length a multiple of 512, output columns a multiple of 32).
+ *   The plan depends on the descriptor only (the rows per expert enter through
+ *   their mean, T*K/E).  Errors: as moe_workspace_bytes; MOE_EINVAL if plan
+ *   is NULL.
+ */
+moe_status moe_gemm_plan(const moe_desc* d, int32_t* plan);
+
 #ifdef __cplusplus
 }
 #endif

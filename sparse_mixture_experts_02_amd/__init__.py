@@ -102,6 +102,8 @@ def load_library():
         lib.moe_probe_mfma_flops.restype = ctypes.c_int64
         lib.moe_probe_read.argtypes = [P, ctypes.c_int64, I32, P, P]
         lib.moe_probe_read.restype = ctypes.c_int
+        lib.moe_gemm_plan.argtypes = [D, P]
+        lib.moe_gemm_plan.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -127,6 +129,25 @@ def moe_probe_mfma_flops(blocks, iters) -> int:
 def moe_probe_read(buf, nbytes, blocks, out, stream) -> int:
     """Raw call of the HBM read-rate probe; returns the status code."""
     return load_library().moe_probe_read(buf, int(nbytes), int(blocks), out, stream)
+
+
+GEMM_VARIANTS = {0: "generic_m128", 1: "direct_m256_tail", 2: "direct_m128", 3: "direct_m32", 4: "generic_m64",
+                 5: "stream_m32"}
+
+
+def moe_gemm_plan(desc: MoeDesc) -> dict:
+    """The two grouped GEMMs a call with `desc` runs (host only, no device
+    call): per GEMM the kernel variant, rows and columns per tile, column
+    tiles, whether its last round may be split along K, and the work-list
+    capacity."""
+    buf = (ctypes.c_int32 * 12)()
+    _check(load_library().moe_gemm_plan(ctypes.byref(desc), buf))
+    out = {}
+    for i, name in enumerate(("gate_up", "down")):
+        v = list(buf[6 * i:6 * i + 6])
+        out[name] = dict(variant=GEMM_VARIANTS.get(v[0], str(v[0])), rows=v[1], cols=v[2], col_tiles=v[3],
+                         k_split=bool(v[4]), max_items=v[5])
+    return out
 
 
 def moe_workspace_bytes(desc: MoeDesc) -> int:
@@ -403,4 +424,5 @@ MOE_STAGE_EVENTS = 6
 __all__ = ["MoeDesc", "MoeRouting", "MoEError", "load_library", "moe_forward", "moe_forward_noalloc",
            "moe_forward_timed",
            "moe_forward_routed", "moe_dispatch", "moe_dispatch_routed", "moe_workspace_bytes", "moe_status_string",
-           "moe_abi_version", "make_desc", "stats_len", "forward", "dispatch", "LIB_PATH"]
+           "moe_abi_version", "moe_gemm_plan", "GEMM_VARIANTS", "make_desc", "stats_len", "forward", "dispatch",
+           "LIB_PATH"]

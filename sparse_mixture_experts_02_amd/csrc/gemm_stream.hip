@@ -1,0 +1,319 @@
+// Weight-streaming grouped GEMM for decode-sized expert segments (bf16, at
+// most 32 rows per expert tile): the gate_up and down projections when each
+// expert holds only a few tokens, so the product is bound by reading the
+// active experts' weights once from HBM (the Dew "Mixture of experts" page,
+// section "Expert computation and placement": the sorted rows of each expert
+// run as one grouped product; epilogues as in gemm_epilogue.h).
+//
+// Tile: up to 32 sorted rows x 256 weight rows (SwiGLU: 128 gate rows and the
+// 128 matching up rows -> 128 h columns), as the 32-row tile of gemm_bf16.hip,
+// with the same work lists and K split.  What differs is the order in which
+// the weights are read.  HBM serves a weight tile read as 32 rows x 1 KB per
+// step about a fifth faster than as 256 rows x 128 bytes per step (a read
+// probe over the Mixtral-shaped gate_up weights: 6.26 against 5.2 TB/s): the
+// long runs stay in the DRAM pages they open.  So the K range is walked in
+// chunks of 512 (1 KB of every row) and each chunk in eight stages of one
+// 32-row weight strip (32 KB, one 1 KB row per load instruction).  The four
+// waves split each chunk along K (128 each) and hold partial sums for all
+// eight strips; they meet once, in LDS, at the end of the tile, summed in wave
+// order (reproducible).  The activation rows of a chunk (32 rows x 1 KB) go to
+// an LDS buffer of their own, loaded once per chunk during its second stage.
+//
+// LDS: the activation buffer (32 KB) and four weight stages (4 x 32 KB); rows
+// are 1 KB with the 16-byte chunk index XOR-ed with the row's low four bits,
+// so the 32 rows of a fragment read fall on distinct banks in each
+// 16-lane phase.
+//
+// Requires bf16, K a multiple of 512 and operands under 4 GiB of byte offsets
+// (the host plan selects this kernel only then).
+#include <type_traits>
+
+#include "gemm_epilogue.h"
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ void lds_dma16(const char* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// Wait until at most N vector-memory loads of this wave are in flight and
+// all of its LDS reads have returned (so no read of a stage can still be
+// pending when the barrier that follows frees its buffer for new loads).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
+
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
+
+constexpr int kKC = kStreamChunk;  // k per chunk: 1 KB of every bf16 row
+constexpr int kRowB = kKC * 2;      // bytes per LDS row
+constexpr int kStrip = 32;          // weight rows per stage
+constexpr int kStrips = 8;          // stages per chunk (256 weight rows)
+constexpr int kStages = 5;          // weight stages in LDS (160 KB)
+constexpr int kStageB = kStrip * kRowB;  // 32 KB
+constexpr int kLoads = kStrip / 4;  // load instructions per wave per stage (one row each)
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
+  using elem = uint16_t;
+  constexpr bool DUAL = EPI == EPI_SWIGLU;
+  constexpr int OUTC = DUAL ? 128 : 256;
+  constexpr int BM = 32;
+  // LDS: weight stages 0..4; reused at the end for the four waves' partial
+  // sums (4 x 32 KB).
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageB];
+  char* const bbuf = lds;
+
+  if ((int)blockIdx.x >= a.num_work[0]) return;
+  const int nch = (int)(a.Kd / kKC);
+  constexpr bool SPLITTABLE = EPI != EPI_DOWN_ATOMIC;
+  int2 wk = a.work[blockIdx.x];
+  int c0 = 0, c1 = nch, split_slot = -1;
+  if constexpr (SPLITTABLE) {
+    if (item_is_split(wk)) {
+      // part p of P covers chunks [p*nch/P, (p+1)*nch/P): any partition of
+      // the K range is summed by the fix-up
+      const int P = a.split_info[1];
+      int j, p;
+      split_part(wk, P, &j, &p);
+      wk = a.split_tiles[j];
+      split_k_range(p, P, nch, &c0, &c1);
+      split_slot = j * P + p;
+    }
+  }
+  const int e = item_expert(wk);
+  const int r0 = item_first_row(wk);
+  const int rows = item_rows(a.offsets[e + 1] - r0, false, BM, 0);
+  const int64_t n0 = (int64_t)item_col_tile(wk) * OUTC;
+  const int64_t N = a.N;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+
+  // Activations go straight to registers as MFMA fragments: lane (l32, h)
+  // of wave w holds, for 16-k slice s of the wave's quarter of a chunk, the
+  // 8 elements of sorted row l32 at chunk-local 16-byte chunk 16w + 2s + h
+  // (rows past the segment repeat its first row).  They are small and read
+  // by every tile of the expert, so they come from L2.
+  const char* arow;
+  {
+    const int r = r0 + (l32 < rows ? l32 : 0);
+    const int64_t src = a.a_index ? (int64_t)a.a_index[r] : (int64_t)r;
+    arow = static_cast<const char*>(a.A) + src * a.lda * 2 + (16 * w + h) * 16;
+  }
+  auto load_a = [&](bf16x8* f, int c) {
+    const char* p = arow + (int64_t)c * kRowB;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) f[s] = *reinterpret_cast<const bf16x8*>(p + 32 * s);
+  };
+
+  // Weights.  Wave w fills rows 8w .. 8w+7 of a 32-row stage, one 1 KB row
+  // per instruction; lane l writes LDS bytes [16l, 16l+16) of the row, which
+  // hold the row's 16-byte chunk l ^ (row & 15).
+  const char* Bbase = static_cast<const char*>(a.B) + (int64_t)e * a.b_estride * 2;
+  // First weight row of strip j.  N is a multiple of 32 (the host selects
+  // this kernel only then), so a strip lies wholly inside or wholly past the
+  // N output rows; one past them re-reads the last strip (its sums are not
+  // stored).
+  auto strip_row = [&](int j) -> int64_t {
+    if constexpr (DUAL) {
+      const int64_t nn = n0 + (j & 3) * kStrip;
+      return (nn < N ? nn : N - kStrip) + (j >= 4 ? a.up_off : 0);
+    } else {
+      const int64_t nn = n0 + j * kStrip;
+      return nn < N ? nn : N - kStrip;
+    }
+  };
+  // per-lane byte offsets of this wave's rows inside a strip: row 8w + q
+  const int64_t ldb_b = a.ldb * 2;
+  uint32_t boff[kLoads];
+#pragma unroll
+  for (int q = 0; q < kLoads; ++q)
+    boff[q] = (uint32_t)((8 * w + q) * ldb_b) + (uint32_t)((lane ^ ((8 * w + q) & 15)) * 16);
+  // stage st (0-based in this item) = strip st % 8 of chunk c0 + st / 8, in
+  // LDS buffer st % kStages
+  auto issue_b = [&](int st, int buf) {
+    const int j = st & (kStrips - 1);
+    const char* src = Bbase + strip_row(j) * ldb_b + (int64_t)(c0 + st / kStrips) * kRowB;
+    char* dst = bbuf + buf * kStageB;
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) lds_dma16(src + boff[q], dst + (8 * w + q) * kRowB);
+  };
+  // weight fragment of slice s: row l32, logical chunk 16w + 2s + h
+  auto frag = [&](const char* buf, int s) {
+    const int ch = (16 * w + 2 * s + h) ^ (l32 & 15);
+    return *reinterpret_cast<const bf16x8*>(buf + l32 * kRowB + ch * 16);
+  };
+
+  f32x16 acc[kStrips];
+#pragma unroll
+  for (int j = 0; j < kStrips; ++j) acc[j] = f32x16{};
+  bf16x8 af[8], an[8];
+
+  const int nst = (c1 - c0) * kStrips;  // >= 8
+  // Prologue: the first chunk's activations, then weight stages 0..3.
+  load_a(af, c0);
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t) issue_b(t, t);
+  int rb = 0;  // LDS buffer of the current stage (st % kStages)
+
+  // Stage st: wait for this wave's loads of stage st, barrier (stage st
+  // visible to all waves, all waves done with stage st-1), issue stage st+4
+  // into stage st-1's buffer, read the eight weight fragments, 8 MFMAs.  At
+  // the second stage of a chunk the next chunk's activations are loaded into
+  // registers (used from its first stage on).  WAIT: this wave's loads issued
+  // after stage st's, which may stay in flight:
+  //   stage j of a chunk   later loads
+  //   0, 1, 6, 7           weights of st+1 .. st+3 (24)
+  //   2 .. 5               the same and the next chunk's activations (32;
+  //                        issued at stage 1 after the weights of st+4 there)
+  // and in the last chunk, whose stages 4..7 issue nothing: 24 for stages
+  // 0..4, then 16, 8, 0.
+  // cur: this chunk's activation fragments; nxt: the next chunk's, loaded
+  // here (two register sets that swap roles chunk by chunk, so no copy ever
+  // waits for a load)
+  auto stage = [&](int st, bf16x8 (&cur)[8], bf16x8 (&nxt)[8], auto J_, auto ISSUE_, auto NEXTA_, auto WAIT_) {
+    constexpr int J = decltype(J_)::value, WAIT = decltype(WAIT_)::value;
+    constexpr bool ISSUE = decltype(ISSUE_)::value, NEXTA = decltype(NEXTA_)::value;
+    wait_vm<WAIT>();
+    barrier_lds();
+    if constexpr (ISSUE) issue_b(st + kStages - 1, rb == 0 ? kStages - 1 : rb - 1);
+    if constexpr (NEXTA) load_a(nxt, c0 + st / kStrips + 1);
+    // all eight weight fragments first: one LDS round trip per stage
+    const char* buf = bbuf + rb * kStageB;
+    bf16x8 bf[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) bf[s] = frag(buf, s);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc[J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[s], cur[s], acc[J], 0, 0, 0);
+    rb = rb == kStages - 1 ? 0 : rb + 1;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  using I6 = std::integral_constant<int, 6>;
+  using I7 = std::integral_constant<int, 7>;
+  using W0 = std::integral_constant<int, 0>;
+  using W8 = std::integral_constant<int, kLoads>;
+  using W16 = std::integral_constant<int, 2 * kLoads>;
+  using W24 = std::integral_constant<int, 3 * kLoads>;
+  using W32 = std::integral_constant<int, 4 * kLoads>;
+  constexpr std::true_type Y{};
+  constexpr std::false_type Nn{};
+  // a chunk that is not the last: every stage issues stage st+4, which exists
+  auto chunk = [&](int st, bf16x8 (&cur)[8], bf16x8 (&nxt)[8]) {
+    stage(st + 0, cur, nxt, I0{}, Y, Nn, W24{});
+    stage(st + 1, cur, nxt, I1{}, Y, Y, W24{});
+    stage(st + 2, cur, nxt, I2{}, Y, Nn, W32{});
+    stage(st + 3, cur, nxt, I3{}, Y, Nn, W32{});
+    stage(st + 4, cur, nxt, I4{}, Y, Nn, W32{});
+    stage(st + 5, cur, nxt, I5{}, Y, Nn, W32{});
+    stage(st + 6, cur, nxt, I6{}, Y, Nn, W24{});
+    stage(st + 7, cur, nxt, I7{}, Y, Nn, W24{});
+  };
+  // the last chunk: no next activations; stages 4..7 issue nothing
+  auto last_chunk = [&](int st, bf16x8 (&cur)[8], bf16x8 (&nxt)[8]) {
+    stage(st + 0, cur, nxt, I0{}, Y, Nn, W24{});
+    stage(st + 1, cur, nxt, I1{}, Y, Nn, W24{});
+    stage(st + 2, cur, nxt, I2{}, Y, Nn, W24{});
+    stage(st + 3, cur, nxt, I3{}, Y, Nn, W24{});
+    stage(st + 4, cur, nxt, I4{}, Nn, Nn, W24{});
+    stage(st + 5, cur, nxt, I5{}, Nn, Nn, W16{});
+    stage(st + 6, cur, nxt, I6{}, Nn, Nn, W8{});
+    stage(st + 7, cur, nxt, I7{}, Nn, Nn, W0{});
+  };
+  int st = 0;
+  for (; st + 2 * kStrips < nst; st += 2 * kStrips) {
+    chunk(st, af, an);
+    chunk(st + kStrips, an, af);
+  }
+  if (st + kStrips < nst) {
+    chunk(st, af, an);
+    last_chunk(st + kStrips, an, af);
+  } else {
+    last_chunk(st, af, an);
+  }
+
+  // The four waves' partial sums meet in LDS (all loads have landed and every
+  // wave is past its last fragment read once the barrier is crossed).
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  barrier_lds();
+  float* part = reinterpret_cast<float*>(lds);  // [wave][strip][16][64]
+#pragma unroll
+  for (int j = 0; j < kStrips; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[((w * kStrips + j) * 16 + r) * 64 + lane] = acc[j][r];
+  __syncthreads();
+  // wave w finishes strips (DUAL) w and w+4: the gate and up sums of h
+  // columns 32w ..; otherwise 2w and 2w+1
+  auto sum4 = [&](int j) {
+    f32x16 v = f32x16{};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] += part[((u * kStrips + j) * 16 + r) * 64 + lane];
+    return v;
+  };
+  const int ja = DUAL ? w : 2 * w, jb = DUAL ? w + 4 : 2 * w + 1;
+  const f32x16 s0 = sum4(ja), s1 = sum4(jb);
+  const int m = l32;
+  if (m >= rows) return;
+  if constexpr (SPLITTABLE) {
+    if (split_slot >= 0) {
+      // raw fp32 partial sums, tile-local rows x 256 columns (SwiGLU: gate
+      // sums in [0,128), up sums in [128,256)), as the other tiles store them
+      float* dst = a.partial + (int64_t)split_slot * a.split_rows * kSplitTileCols + m * kSplitTileCols;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c = 8 * q4 + 4 * h;
+        *reinterpret_cast<float4*>(dst + ja * kStrip + c) = float4{s0[4 * q4], s0[4 * q4 + 1], s0[4 * q4 + 2], s0[4 * q4 + 3]};
+        *reinterpret_cast<float4*>(dst + jb * kStrip + c) = float4{s1[4 * q4], s1[4 * q4 + 1], s1[4 * q4 + 2], s1[4 * q4 + 3]};
+      }
+      return;
+    }
+  }
+  const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;
+  const RowCtx rc = row_ctx<EPI>(a, r0 + m);
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const f32x4 v0{s0[4 * q4], s0[4 * q4 + 1], s0[4 * q4 + 2], s0[4 * q4 + 3]};
+    const f32x4 v1{s1[4 * q4], s1[4 * q4 + 1], s1[4 * q4 + 2], s1[4 * q4 + 3]};
+    if constexpr (DUAL) {
+      epilogue4<elem, EPI>(a, rc, n0 + ja * kStrip + 8 * q4 + 4 * h, v0, v1, bias);
+    } else {
+      epilogue4<elem, EPI>(a, rc, n0 + ja * kStrip + 8 * q4 + 4 * h, v0, v0, bias);
+      epilogue4<elem, EPI>(a, rc, n0 + jb * kStrip + 8 * q4 + 4 * h, v1, v1, bias);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_stream(int epi, const GemmArgs& a, hipStream_t s) {
+  switch (epi) {
+    case EPI_SWIGLU:
+      hipLaunchKernelGGL((gemm_stream_kernel<EPI_SWIGLU>), dim3(a.max_work), dim3(256), 0, s, a);
+      break;
+    case EPI_RELU:
+      hipLaunchKernelGGL((gemm_stream_kernel<EPI_RELU>), dim3(a.max_work), dim3(256), 0, s, a);
+      break;
+    case EPI_DOWN_ATOMIC:
+      hipLaunchKernelGGL((gemm_stream_kernel<EPI_DOWN_ATOMIC>), dim3(a.max_work), dim3(256), 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm_stream_kernel<EPI_DOWN_SLOT>), dim3(a.max_work), dim3(256), 0, s, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -11,6 +11,7 @@
 #include <mutex>
 
 #include "moe_common.h"
+#include "moe_probes.h"
 
 // Workspace of moe_forward_noalloc: one copy per device, held from the first
 // call on that device until the process ends.  Host code never passes this
@@ -80,6 +81,9 @@ GemmPlan plan_gemm(const moe_desc* d, int64_t M, int64_t N, int64_t Kd, int64_t 
   if (direct_ok) {
     const int64_t mean = M / d->E;
     p.var = mean >= 512 ? VAR_BF16_M256 : (mean >= 64 ? VAR_BF16_M128 : VAR_BF16_M32);
+    // decode-sized bf16 segments: the weight-streaming kernel, which reads
+    // every weight row in 1 KB runs
+    if (p.var == VAR_BF16_M32 && d->dtype == MOE_BF16 && Kd % kStreamChunk == 0 && N % 32 == 0) p.var = VAR_BF16_S32;
   } else {
     // Generic kernel: 64-row tiles when 128-row ones would not fill two
     // rounds of a 256-CU part (a fixed count, so the workspace size does not
@@ -118,6 +122,7 @@ Layout layout_of(const moe_desc* d) {
   // (the tiny fp32 block has 2 K steps per GEMM).
   const int eb = elem_bytes(d->dtype);
   auto splits = [&](int var, int64_t Kd) {
+    if (var == VAR_BF16_S32) return Kd / kStreamChunk >= kMaxSplitParts;  // K steps of 512
     return (var == VAR_BF16_M256 || var == VAR_BF16_M32) && Kd * eb / 128 >= kMaxSplitParts;
   };
   L.split1 = splits(L.g1.var, D);
@@ -586,6 +591,25 @@ moe_status moe_dispatch_routed(const moe_desc* d, const moe_routing* r, const vo
                                void* stream) {
   return dispatch_impl(d, r, x, router, router_bias, selected_experts, routing_weights, router_logits,
                        expert_counts, expert_offsets, sorted_token, sorted_slot, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_gemm_plan(const moe_desc* d, int32_t* plan) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (!plan) return MOE_EINVAL;
+  const Layout L = layout_of(d);
+  const GemmPlan* g[2] = {&L.g1, &L.g2};
+  const bool split[2] = {L.split1, L.split2};
+  for (int i = 0; i < 2; ++i) {
+    int32_t* o = plan + 6 * i;
+    o[0] = g[i]->var;
+    o[1] = g[i]->bm;
+    o[2] = g[i]->cols;
+    o[3] = g[i]->ntn;
+    o[4] = split[i] ? 1 : 0;
+    o[5] = g[i]->max_work;
+  }
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -161,7 +161,14 @@ enum Epilogue { EPI_SWIGLU = 0, EPI_RELU = 1, EPI_DOWN_ATOMIC = 2, EPI_DOWN_SLOT
 //            (whole 128-byte stages), 16-byte aligned rows; LDS stages filled
 //            by direct global->LDS loads; xxx rows per tile (256 and 128 for
 //            prefill, 32 for decode-sized segments).
-enum Variant { VAR_GENERIC = 0, VAR_BF16_M256 = 1, VAR_BF16_M128 = 2, VAR_BF16_M32 = 3, VAR_GENERIC_M64 = 4 };
+enum Variant {
+  VAR_GENERIC = 0,
+  VAR_BF16_M256 = 1,
+  VAR_BF16_M128 = 2,
+  VAR_BF16_M32 = 3,
+  VAR_GENERIC_M64 = 4,
+  VAR_BF16_S32 = 5,  // weight-streaming 32-row tiles (gemm_stream.hip): bf16, K a multiple of 512
+};
 int variant_rows(int var);
 int variant_cols(int var, bool dual);
 
@@ -205,6 +212,9 @@ constexpr int kSplitTileCols = 256;  // columns of a partial tile (rows: GemmArg
 hipError_t launch_split_fixup(int dtype, int epi, const GemmArgs& a, int32_t ncu, hipStream_t s);
 // The direct-to-LDS variants (VAR_BF16_*) for dtype 1 (bf16) or 0 (fp32).
 hipError_t launch_gemm_bf16(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s);
+// The weight-streaming variant (VAR_BF16_S32, bf16 only).
+constexpr int kStreamChunk = 512;  // K elements per chunk of the weight-streaming kernel
+hipError_t launch_gemm_stream(int epi, const GemmArgs& a, hipStream_t s);
 
 struct FinalizeArgs {
   const float* src;   // slot rows (T*K, D) when K > 0 slots, or (T, D) accumulation

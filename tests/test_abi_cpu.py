@@ -222,3 +222,45 @@ def test_noalloc_refuses_oversize_before_any_launch(lib):
     assert moe.moe_forward_noalloc(_desc(K=0), fake, fake, fake, fake, None, None, None, fake, fake, fake, None,
                                    None, None) == moe.MOE_EINVAL
     assert moe.moe_forward_noalloc(_desc(T=0), *([None] * 12), None) == moe.MOE_OK
+
+
+@pytest.mark.parametrize("kw,g1,g2", [
+    # the Mixtral-shaped prefill: 2048 rows per expert -> 256-row tiles with tail strips
+    (dict(T=8192, D=4096, F=14336, E=8, K=2, dtype=1), "direct_m256_tail", "direct_m256_tail"),
+    # the 64-token decode batch: 16 rows per expert, bf16, K a multiple of 512 -> weight streaming
+    (dict(T=64, D=4096, F=14336, E=8, K=2, dtype=1), "stream_m32", "stream_m32"),
+    # the same in fp32: the direct 32-row tiles
+    (dict(T=64, D=4096, F=14336, E=8, K=2, dtype=0), "direct_m32", "direct_m32"),
+    # gate_up contracts over D = 768 (not a multiple of 512), down over F = 1024
+    (dict(T=64, D=768, F=1024, E=8, K=2, dtype=1), "direct_m32", "stream_m32"),
+    # gate_up's 1040 output columns are a multiple of 16 but not of 32; down
+    # contracts over 1040 (not whole 128-byte stages) -> the generic kernel
+    (dict(T=64, D=1024, F=1040, E=8, K=2, dtype=1), "direct_m32", "generic_m64"),
+    # the 128-expert layer: 1024 rows per expert -> 256-row tiles
+    (dict(T=16384, D=2048, F=768, E=128, K=8, dtype=1), "direct_m256_tail", "direct_m256_tail"),
+    # 128-row tiles between 64 and 512 rows per expert
+    (dict(T=1000, D=512, F=1024, E=8, K=2, dtype=1), "direct_m128", "direct_m128"),
+    # K not filling 128-byte stages -> the generic kernel
+    (dict(T=1000, D=40, F=48, E=8, K=2, dtype=0), "generic_m64", "generic_m64"),
+])
+def test_gemm_plan_picks_the_kernel_for_the_shape(lib, kw, g1, g2):
+    plan = moe.moe_gemm_plan(_desc(**kw))
+    assert plan["gate_up"]["variant"] == g1 and plan["down"]["variant"] == g2, plan
+    for name, N in (("gate_up", kw["F"]), ("down", kw["D"])):
+        p = plan[name]
+        assert p["col_tiles"] == -(-N // p["cols"])
+        assert p["max_items"] >= p["col_tiles"]
+
+
+def test_gemm_plan_k_split_rules(lib):
+    # decode: both streaming GEMMs have >= 8 chunks of 512 along K; the down
+    # GEMM splits only in the deterministic mode
+    det = moe.moe_gemm_plan(_desc(T=64, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=1))
+    atom = moe.moe_gemm_plan(_desc(T=64, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=0))
+    assert det["gate_up"]["k_split"] and det["down"]["k_split"]
+    assert atom["gate_up"]["k_split"] and not atom["down"]["k_split"]
+    # a 3584-long contraction has 7 chunks of 512: no split of the streaming GEMM
+    short = moe.moe_gemm_plan(_desc(T=64, D=3584, F=14336, E=8, K=2, dtype=1, deterministic=1))
+    assert short["gate_up"]["variant"] == "stream_m32" and not short["gate_up"]["k_split"]
+    with pytest.raises(ValueError):
+        moe.moe_gemm_plan(_desc(K=0))

@@ -113,6 +113,7 @@ EDGE = [
     (40, 256, 384, 8, 2, "swiglu", "bf16", False, True),
     (64, 4096, 1024, 8, 2, "swiglu", "bf16", False, True),
     (3000, 64, 128, 40, 6, "swiglu", "bf16", False, True),
+
     # bf16 routers over more than 64 experts with D a multiple of 256 take the
     # LDS-staged logits kernel (64 tokens per block): ragged token blocks,
     # expert counts off the 16-row MFMA tile, a router bias, 8 and 16 tiles
@@ -134,6 +135,37 @@ EDGE_LAST = [
     (2500, 64, 96, 256, 4, "relu", "f32", True, True),
     (700, 256, 320, 65, 2, "swiglu", "bf16", False, True),
 ]
+
+
+# Decode-sized bf16 segments with K a multiple of 512 take the weight-streaming
+# kernel: 1 to 16 K chunks of 512 (odd and even counts, so both ways through
+# its two-chunk loop), K-split parts of two chunks, the ReLU (256-column) and
+# SwiGLU (128-column) tiles, a column tail off the tile width, experts with
+# more than 32 rows.  The last field names the kernels the plan must pick.
+STREAM = [
+    (40, 1024, 1536, 8, 2, "swiglu", "bf16", False, True, ("stream_m32", "stream_m32")),
+    (24, 1536, 2048, 4, 2, "relu", "bf16", True, True, ("stream_m32", "stream_m32")),
+    (16, 8192, 512, 4, 2, "swiglu", "bf16", False, True, ("stream_m32", "stream_m32")),
+    (30, 512, 1056, 8, 2, "swiglu", "bf16", True, False, ("stream_m32", "generic_m64")),
+    (50, 2560, 512, 8, 3, "relu", "bf16", False, True, ("stream_m32", "stream_m32")),
+]
+
+
+@pytest.mark.parametrize("case", STREAM, ids=lambda c: "T%d_D%d_F%d_E%d_K%d_%s_%s_b%d_n%d" % tuple(c[:9]))
+@pytest.mark.parametrize("det", [False, True])
+def test_weight_streaming_shapes(case, det):
+    T, D, F, E, K, act, dt, biases, norm, kernels = case
+    desc = moe.make_desc(T, D, F, E, K, norm_topk_prob=norm, act="silu" if act == "swiglu" else "relu",
+                         dtype=torch.bfloat16, deterministic=det)
+    plan = moe.moe_gemm_plan(desc)
+    assert (plan["gate_up"]["variant"], plan["down"]["variant"]) == kernels, plan
+    cfg = workloads.small_config(T, D, F, E, K, act=act, dtype=dt, norm=norm, biases=biases,
+                                 router_bias="zipf" if E >= 8 else None, cfg_id=500 + E + K)
+    inp = workloads.generate(cfg)
+    _say("stream %s det=%s" % (case[:9], det))
+    g = gpu_forward(inp, deterministic=det)
+    check(inp, g)
+    check_full_properties(inp, g)
 
 
 @pytest.mark.parametrize("case", EDGE, ids=lambda c: "T%d_D%d_F%d_E%d_K%d_%s_%s_b%d_n%d" % tuple(c))
