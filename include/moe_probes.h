@@ -42,8 +42,9 @@ moe_status moe_probe_read(const void* buf, int64_t bytes, int32_t blocks, float*
  *   work items may be split along K (0/1), and the work-list capacity.
  *   Variants: 0 generic 128-row tiles; 1 direct-to-LDS 256-row tiles with
  *   32-row tail strips; 2 direct-to-LDS 128-row tiles; 3 direct-to-LDS 32-row
- *   tiles; 4 generic 64-row tiles; 5 weight-streaming 32-row tiles (bf16,
- *   contraction length a multiple of 512, output columns a multiple of 32).
+ *   tiles; 4 generic 64-row tiles; 5 weight-streaming 32-row tiles of 256
+ *   weight rows (bf16, contraction length a multiple of 512, output columns a
+ *   multiple of 32); 6 the same with 128 weight rows per tile (never split).
  *   The plan depends on the descriptor only (the rows per expert enter through
  *   their mean, T*K/E).  Errors: as moe_workspace_bytes; MOE_EINVAL if plan
  *   is NULL.

@@ -5,27 +5,30 @@
 // section "Expert computation and placement": the sorted rows of each expert
 // run as one grouped product; epilogues as in gemm_epilogue.h).
 //
-// Tile: up to 32 sorted rows x 256 weight rows (SwiGLU: 128 gate rows and the
-// 128 matching up rows -> 128 h columns), as the 32-row tile of gemm_bf16.hip,
-// with the same work lists and K split.  What differs is the order in which
-// the weights are read.  HBM serves a weight tile read as 32 rows x 1 KB per
-// step about a fifth faster than as 256 rows x 128 bytes per step (a read
-// probe over the Mixtral-shaped gate_up weights: 6.26 against 5.2 TB/s): the
-// long runs stay in the DRAM pages they open.  So the K range is walked in
-// chunks of 512 (1 KB of every row) and each chunk in eight stages of one
-// 32-row weight strip (32 KB, one 1 KB row per load instruction).  The four
-// waves split each chunk along K (128 each) and hold partial sums for all
-// eight strips; they meet once, in LDS, at the end of the tile, summed in wave
-// order (reproducible).  The activation rows of a chunk (32 rows x 1 KB) go to
-// an LDS buffer of their own, loaded once per chunk during its second stage.
+// Tile: up to 32 sorted rows x 32*NS weight rows, NS = 8 or 4 strips of 32
+// (SwiGLU: NS/2 gate strips and the matching up strips -> 16*NS h columns).
+// The wide tile (NS = 8) has the shape of gemm_bf16.hip's 32-row tile, with
+// its work lists and K split; the narrow one (NS = 4) has twice the column
+// tiles and never splits (the host takes it when its items fill whole rounds
+// of the CUs, so that no fix-up kernel is needed).  What differs from
+// gemm_bf16.hip is the order in which the weights are read.  HBM serves a
+// weight tile read as 32 rows x 1 KB per step about a fifth faster than as
+// 256 rows x 128 bytes per step (a read probe over the Mixtral-shaped gate_up
+// weights: 6.27 against 5.25 TB/s): the long runs stay in the DRAM pages they
+// open.  So the K range is walked in chunks of 512 (1 KB of every row) and
+// each chunk in NS stages of one 32-row weight strip (32 KB, one 1 KB row per
+// load instruction).  The four waves split each chunk along K (128 each) and
+// hold partial sums for all NS strips; they meet once, in LDS, at the end of
+// the tile, summed in wave order (reproducible).  The activation rows go
+// straight to registers as MFMA fragments (they are small and every tile of
+// an expert reads the same rows, so they come from L2).
 //
-// LDS: the activation buffer (32 KB) and four weight stages (4 x 32 KB); rows
-// are 1 KB with the 16-byte chunk index XOR-ed with the row's low four bits,
-// so the 32 rows of a fragment read fall on distinct banks in each
-// 16-lane phase.
+// LDS: five weight stages of 32 KB; rows are 1 KB with the 16-byte chunk
+// index XOR-ed with the row's low four bits, so the 32 rows of a fragment read
+// fall on distinct banks in each 16-lane phase.
 //
-// Requires bf16, K a multiple of 512 and operands under 4 GiB of byte offsets
-// (the host plan selects this kernel only then).
+// Requires bf16, K a multiple of 512, N a multiple of 32 and operands under
+// 4 GiB of byte offsets (the host plan selects this kernel only then).
 #include <type_traits>
 
 #include "gemm_epilogue.h"
@@ -52,25 +55,28 @@ __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "me
 constexpr int kKC = kStreamChunk;  // k per chunk: 1 KB of every bf16 row
 constexpr int kRowB = kKC * 2;      // bytes per LDS row
 constexpr int kStrip = 32;          // weight rows per stage
-constexpr int kStrips = 8;          // stages per chunk (256 weight rows)
-constexpr int kStages = 5;          // weight stages in LDS (160 KB)
+constexpr int kStages = 5;          // weight stages in LDS (160 KB), four in flight
 constexpr int kStageB = kStrip * kRowB;  // 32 KB
 constexpr int kLoads = kStrip / 4;  // load instructions per wave per stage (one row each)
 
-template <int EPI>
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+template <int EPI, int NS>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
+  static_assert(NS == 8 || NS == 4, "strips per tile");
   using elem = uint16_t;
   constexpr bool DUAL = EPI == EPI_SWIGLU;
-  constexpr int OUTC = DUAL ? 128 : 256;
+  constexpr int OUTC = DUAL ? 16 * NS : 32 * NS;  // output columns per tile
   constexpr int BM = 32;
   // LDS: weight stages 0..4; reused at the end for the four waves' partial
-  // sums (4 x 32 KB).
+  // sums (4 x NS x 4 KB).
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageB];
   char* const bbuf = lds;
 
   if ((int)blockIdx.x >= a.num_work[0]) return;
   const int nch = (int)(a.Kd / kKC);
-  constexpr bool SPLITTABLE = EPI != EPI_DOWN_ATOMIC;
+  constexpr bool SPLITTABLE = EPI != EPI_DOWN_ATOMIC && NS == 8;
   int2 wk = a.work[blockIdx.x];
   int c0 = 0, c1 = nch, split_slot = -1;
   if constexpr (SPLITTABLE) {
@@ -98,8 +104,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   // Activations go straight to registers as MFMA fragments: lane (l32, h)
   // of wave w holds, for 16-k slice s of the wave's quarter of a chunk, the
   // 8 elements of sorted row l32 at chunk-local 16-byte chunk 16w + 2s + h
-  // (rows past the segment repeat its first row).  They are small and read
-  // by every tile of the expert, so they come from L2.
+  // (rows past the segment repeat its first row).
   const char* arow;
   {
     const int r = r0 + (l32 < rows ? l32 : 0);
@@ -116,14 +121,14 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   // per instruction; lane l writes LDS bytes [16l, 16l+16) of the row, which
   // hold the row's 16-byte chunk l ^ (row & 15).
   const char* Bbase = static_cast<const char*>(a.B) + (int64_t)e * a.b_estride * 2;
-  // First weight row of strip j.  N is a multiple of 32 (the host selects
-  // this kernel only then), so a strip lies wholly inside or wholly past the
-  // N output rows; one past them re-reads the last strip (its sums are not
-  // stored).
+  // First weight row of strip j.  N is a multiple of 32, so a strip lies
+  // wholly inside or wholly past the N output rows; one past them re-reads
+  // the last strip (its sums are not stored).  SwiGLU: strips [0, NS/2) are
+  // gate rows, [NS/2, NS) the matching up rows.
   auto strip_row = [&](int j) -> int64_t {
     if constexpr (DUAL) {
-      const int64_t nn = n0 + (j & 3) * kStrip;
-      return (nn < N ? nn : N - kStrip) + (j >= 4 ? a.up_off : 0);
+      const int64_t nn = n0 + (j % (NS / 2)) * kStrip;
+      return (nn < N ? nn : N - kStrip) + (j >= NS / 2 ? a.up_off : 0);
     } else {
       const int64_t nn = n0 + j * kStrip;
       return nn < N ? nn : N - kStrip;
@@ -135,11 +140,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
   for (int q = 0; q < kLoads; ++q)
     boff[q] = (uint32_t)((8 * w + q) * ldb_b) + (uint32_t)((lane ^ ((8 * w + q) & 15)) * 16);
-  // stage st (0-based in this item) = strip st % 8 of chunk c0 + st / 8, in
+  // stage st (0-based in this item) = strip st % NS of chunk c0 + st / NS, in
   // LDS buffer st % kStages
   auto issue_b = [&](int st, int buf) {
-    const int j = st & (kStrips - 1);
-    const char* src = Bbase + strip_row(j) * ldb_b + (int64_t)(c0 + st / kStrips) * kRowB;
+    const int j = st % NS;
+    const char* src = Bbase + strip_row(j) * ldb_b + (int64_t)(c0 + st / NS) * kRowB;
     char* dst = bbuf + buf * kStageB;
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) lds_dma16(src + boff[q], dst + (8 * w + q) * kRowB);
@@ -150,12 +155,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     return *reinterpret_cast<const bf16x8*>(buf + l32 * kRowB + ch * 16);
   };
 
-  f32x16 acc[kStrips];
+  f32x16 acc[NS];
 #pragma unroll
-  for (int j = 0; j < kStrips; ++j) acc[j] = f32x16{};
+  for (int j = 0; j < NS; ++j) acc[j] = f32x16{};
   bf16x8 af[8], an[8];
 
-  const int nst = (c1 - c0) * kStrips;  // >= 8
+  const int nst = (c1 - c0) * NS;  // >= NS
   // Prologue: the first chunk's activations, then weight stages 0..3.
   load_a(af, c0);
 #pragma unroll
@@ -164,26 +169,20 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 
   // Stage st: wait for this wave's loads of stage st, barrier (stage st
   // visible to all waves, all waves done with stage st-1), issue stage st+4
-  // into stage st-1's buffer, read the eight weight fragments, 8 MFMAs.  At
-  // the second stage of a chunk the next chunk's activations are loaded into
-  // registers (used from its first stage on).  WAIT: this wave's loads issued
-  // after stage st's, which may stay in flight:
-  //   stage j of a chunk   later loads
-  //   0, 1, 6, 7           weights of st+1 .. st+3 (24)
-  //   2 .. 5               the same and the next chunk's activations (32;
-  //                        issued at stage 1 after the weights of st+4 there)
-  // and in the last chunk, whose stages 4..7 issue nothing: 24 for stages
-  // 0..4, then 16, 8, 0.
-  // cur: this chunk's activation fragments; nxt: the next chunk's, loaded
-  // here (two register sets that swap roles chunk by chunk, so no copy ever
-  // waits for a load)
+  // into stage st-1's buffer (ISSUE), load the next chunk's activations into
+  // registers (NEXTA; used from that chunk's first stage on), read the eight
+  // weight fragments, 8 MFMAs.  cur: this chunk's activation fragments, nxt:
+  // the next chunk's (two register sets that swap roles chunk by chunk, so no
+  // copy ever waits for a load).  WAIT, in stages of kLoads loads: this
+  // wave's loads issued after stage st's weights that may stay in flight
+  // (the tables at `chunk`).
   auto stage = [&](int st, bf16x8 (&cur)[8], bf16x8 (&nxt)[8], auto J_, auto ISSUE_, auto NEXTA_, auto WAIT_) {
     constexpr int J = decltype(J_)::value, WAIT = decltype(WAIT_)::value;
     constexpr bool ISSUE = decltype(ISSUE_)::value, NEXTA = decltype(NEXTA_)::value;
-    wait_vm<WAIT>();
+    wait_vm<WAIT * kLoads>();
     barrier_lds();
     if constexpr (ISSUE) issue_b(st + kStages - 1, rb == 0 ? kStages - 1 : rb - 1);
-    if constexpr (NEXTA) load_a(nxt, c0 + st / kStrips + 1);
+    if constexpr (NEXTA) load_a(nxt, c0 + st / NS + 1);
     // all eight weight fragments first: one LDS round trip per stage
     const char* buf = bbuf + rb * kStageB;
     bf16x8 bf[8];
@@ -194,51 +193,65 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     for (int s = 0; s < 8; ++s) acc[J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[s], cur[s], acc[J], 0, 0, 0);
     rb = rb == kStages - 1 ? 0 : rb + 1;
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  using I4 = std::integral_constant<int, 4>;
-  using I5 = std::integral_constant<int, 5>;
-  using I6 = std::integral_constant<int, 6>;
-  using I7 = std::integral_constant<int, 7>;
-  using W0 = std::integral_constant<int, 0>;
-  using W8 = std::integral_constant<int, kLoads>;
-  using W16 = std::integral_constant<int, 2 * kLoads>;
-  using W24 = std::integral_constant<int, 3 * kLoads>;
-  using W32 = std::integral_constant<int, 4 * kLoads>;
   constexpr std::true_type Y{};
   constexpr std::false_type Nn{};
-  // a chunk that is not the last: every stage issues stage st+4, which exists
+  // Wait counts, in stages: the loads issued after stage st's weights.  Issue
+  // order per stage t: the weights of t+4, then (NEXTA) the next chunk's
+  // activations (kLoads loads as well).
+  // NS = 8, activations at stage 1 of a chunk (after the weights of stage 5):
+  //   stage j   0, 1, 6, 7: weights st+1..st+3 (3); 2..5: those and the
+  //             activations (4).  At stage 0 this chunk's activations,
+  //             issued before the weights of stage 0 itself, have landed.
+  //   last chunk (no activations; stages 4..7 issue nothing): 3 for 0..4,
+  //             then 2, 1, 0.
+  // NS = 4, activations at stage 0 of a chunk (after the weights of stage 4):
+  //   stage j   0: weights st+1..st+3 (3; the activations issued after stage
+  //             0's weights are this chunk's own, so they have landed too);
+  //             1..3: those and the activations (4).
+  //   last chunk (its stages issue nothing): 3, 2, 1, 0.
+  // A chunk that is not the last: every stage issues stage st+4, which exists.
   auto chunk = [&](int st, bf16x8 (&cur)[8], bf16x8 (&nxt)[8]) {
-    stage(st + 0, cur, nxt, I0{}, Y, Nn, W24{});
-    stage(st + 1, cur, nxt, I1{}, Y, Y, W24{});
-    stage(st + 2, cur, nxt, I2{}, Y, Nn, W32{});
-    stage(st + 3, cur, nxt, I3{}, Y, Nn, W32{});
-    stage(st + 4, cur, nxt, I4{}, Y, Nn, W32{});
-    stage(st + 5, cur, nxt, I5{}, Y, Nn, W32{});
-    stage(st + 6, cur, nxt, I6{}, Y, Nn, W24{});
-    stage(st + 7, cur, nxt, I7{}, Y, Nn, W24{});
+    if constexpr (NS == 8) {
+      stage(st + 0, cur, nxt, IC<0>{}, Y, Nn, IC<3>{});
+      stage(st + 1, cur, nxt, IC<1>{}, Y, Y, IC<3>{});
+      stage(st + 2, cur, nxt, IC<2>{}, Y, Nn, IC<4>{});
+      stage(st + 3, cur, nxt, IC<3>{}, Y, Nn, IC<4>{});
+      stage(st + 4, cur, nxt, IC<4>{}, Y, Nn, IC<4>{});
+      stage(st + 5, cur, nxt, IC<5>{}, Y, Nn, IC<4>{});
+      stage(st + 6, cur, nxt, IC<6>{}, Y, Nn, IC<3>{});
+      stage(st + 7, cur, nxt, IC<7>{}, Y, Nn, IC<3>{});
+    } else {
+      stage(st + 0, cur, nxt, IC<0>{}, Y, Y, IC<3>{});
+      stage(st + 1, cur, nxt, IC<1>{}, Y, Nn, IC<4>{});
+      stage(st + 2, cur, nxt, IC<2>{}, Y, Nn, IC<4>{});
+      stage(st + 3, cur, nxt, IC<3>{}, Y, Nn, IC<4>{});
+    }
   };
-  // the last chunk: no next activations; stages 4..7 issue nothing
   auto last_chunk = [&](int st, bf16x8 (&cur)[8], bf16x8 (&nxt)[8]) {
-    stage(st + 0, cur, nxt, I0{}, Y, Nn, W24{});
-    stage(st + 1, cur, nxt, I1{}, Y, Nn, W24{});
-    stage(st + 2, cur, nxt, I2{}, Y, Nn, W24{});
-    stage(st + 3, cur, nxt, I3{}, Y, Nn, W24{});
-    stage(st + 4, cur, nxt, I4{}, Nn, Nn, W24{});
-    stage(st + 5, cur, nxt, I5{}, Nn, Nn, W16{});
-    stage(st + 6, cur, nxt, I6{}, Nn, Nn, W8{});
-    stage(st + 7, cur, nxt, I7{}, Nn, Nn, W0{});
+    if constexpr (NS == 8) {
+      stage(st + 0, cur, nxt, IC<0>{}, Y, Nn, IC<3>{});
+      stage(st + 1, cur, nxt, IC<1>{}, Y, Nn, IC<3>{});
+      stage(st + 2, cur, nxt, IC<2>{}, Y, Nn, IC<3>{});
+      stage(st + 3, cur, nxt, IC<3>{}, Y, Nn, IC<3>{});
+      stage(st + 4, cur, nxt, IC<4>{}, Nn, Nn, IC<3>{});
+      stage(st + 5, cur, nxt, IC<5>{}, Nn, Nn, IC<2>{});
+      stage(st + 6, cur, nxt, IC<6>{}, Nn, Nn, IC<1>{});
+      stage(st + 7, cur, nxt, IC<7>{}, Nn, Nn, IC<0>{});
+    } else {
+      stage(st + 0, cur, nxt, IC<0>{}, Nn, Nn, IC<3>{});
+      stage(st + 1, cur, nxt, IC<1>{}, Nn, Nn, IC<2>{});
+      stage(st + 2, cur, nxt, IC<2>{}, Nn, Nn, IC<1>{});
+      stage(st + 3, cur, nxt, IC<3>{}, Nn, Nn, IC<0>{});
+    }
   };
   int st = 0;
-  for (; st + 2 * kStrips < nst; st += 2 * kStrips) {
+  for (; st + 2 * NS < nst; st += 2 * NS) {
     chunk(st, af, an);
-    chunk(st + kStrips, an, af);
+    chunk(st + NS, an, af);
   }
-  if (st + kStrips < nst) {
+  if (st + NS < nst) {
     chunk(st, af, an);
-    last_chunk(st + kStrips, an, af);
+    last_chunk(st + NS, an, af);
   } else {
     last_chunk(st, af, an);
   }
@@ -248,23 +261,29 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   __builtin_amdgcn_s_waitcnt(0xc07f);
   barrier_lds();
   float* part = reinterpret_cast<float*>(lds);  // [wave][strip][16][64]
+  static_assert(4 * NS * 16 * 64 * 4 <= kStages * kStageB, "wave sums fit the stages");
 #pragma unroll
-  for (int j = 0; j < kStrips; ++j)
+  for (int j = 0; j < NS; ++j)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part[((w * kStrips + j) * 16 + r) * 64 + lane] = acc[j][r];
+    for (int r = 0; r < 16; ++r) part[((w * NS + j) * 16 + r) * 64 + lane] = acc[j][r];
   __syncthreads();
-  // wave w finishes strips (DUAL) w and w+4: the gate and up sums of h
-  // columns 32w ..; otherwise 2w and 2w+1
   auto sum4 = [&](int j) {
     f32x16 v = f32x16{};
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] += part[((u * kStrips + j) * 16 + r) * 64 + lane];
+      for (int r = 0; r < 16; ++r) v[r] += part[((u * NS + j) * 16 + r) * 64 + lane];
     return v;
   };
-  const int ja = DUAL ? w : 2 * w, jb = DUAL ? w + 4 : 2 * w + 1;
-  const f32x16 s0 = sum4(ja), s1 = sum4(jb);
+  // Strips each wave finishes.  SwiGLU: the gate and up strips of h columns
+  // 32i .. 32i+31 (strips i and i + NS/2) for i = w (NS = 4: waves 0 and 1
+  // only).  Otherwise strips 2w and 2w+1 (NS = 8) or strip w (NS = 4).
+  constexpr int NPW = DUAL ? 1 : NS / 4;  // output strips per wave
+  if (DUAL && w >= NS / 2) return;
+  const int ja = DUAL ? w : NPW * w;
+  const int jb = DUAL ? w + NS / 2 : NPW * w + NPW - 1;
+  const f32x16 s0 = sum4(ja);
+  const f32x16 s1 = (DUAL || NPW == 2) ? sum4(jb) : s0;
   const int m = l32;
   if (m >= rows) return;
   if constexpr (SPLITTABLE) {
@@ -275,8 +294,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int c = 8 * q4 + 4 * h;
-        *reinterpret_cast<float4*>(dst + ja * kStrip + c) = float4{s0[4 * q4], s0[4 * q4 + 1], s0[4 * q4 + 2], s0[4 * q4 + 3]};
-        *reinterpret_cast<float4*>(dst + jb * kStrip + c) = float4{s1[4 * q4], s1[4 * q4 + 1], s1[4 * q4 + 2], s1[4 * q4 + 3]};
+        *reinterpret_cast<float4*>(dst + ja * kStrip + c) =
+            float4{s0[4 * q4], s0[4 * q4 + 1], s0[4 * q4 + 2], s0[4 * q4 + 3]};
+        *reinterpret_cast<float4*>(dst + jb * kStrip + c) =
+            float4{s1[4 * q4], s1[4 * q4 + 1], s1[4 * q4 + 2], s1[4 * q4 + 3]};
       }
       return;
     }
@@ -291,29 +312,36 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
       epilogue4<elem, EPI>(a, rc, n0 + ja * kStrip + 8 * q4 + 4 * h, v0, v1, bias);
     } else {
       epilogue4<elem, EPI>(a, rc, n0 + ja * kStrip + 8 * q4 + 4 * h, v0, v0, bias);
-      epilogue4<elem, EPI>(a, rc, n0 + jb * kStrip + 8 * q4 + 4 * h, v1, v1, bias);
+      if constexpr (NPW == 2) epilogue4<elem, EPI>(a, rc, n0 + jb * kStrip + 8 * q4 + 4 * h, v1, v1, bias);
     }
   }
 }
 
-}  // namespace
-
-hipError_t launch_gemm_stream(int epi, const GemmArgs& a, hipStream_t s) {
+template <int NS>
+hipError_t launch_ns(int epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
     case EPI_SWIGLU:
-      hipLaunchKernelGGL((gemm_stream_kernel<EPI_SWIGLU>), dim3(a.max_work), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_stream_kernel<EPI_SWIGLU, NS>), dim3(a.max_work), dim3(256), 0, s, a);
       break;
     case EPI_RELU:
-      hipLaunchKernelGGL((gemm_stream_kernel<EPI_RELU>), dim3(a.max_work), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_stream_kernel<EPI_RELU, NS>), dim3(a.max_work), dim3(256), 0, s, a);
       break;
     case EPI_DOWN_ATOMIC:
-      hipLaunchKernelGGL((gemm_stream_kernel<EPI_DOWN_ATOMIC>), dim3(a.max_work), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_stream_kernel<EPI_DOWN_ATOMIC, NS>), dim3(a.max_work), dim3(256), 0, s, a);
       break;
     default:
-      hipLaunchKernelGGL((gemm_stream_kernel<EPI_DOWN_SLOT>), dim3(a.max_work), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_stream_kernel<EPI_DOWN_SLOT, NS>), dim3(a.max_work), dim3(256), 0, s, a);
       break;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_stream(int epi, int strips, const GemmArgs& a, hipStream_t s) {
+  if (strips == 8) return launch_ns<8>(epi, a, s);
+  if (strips == 4) return launch_ns<4>(epi, a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

@@ -71,8 +71,9 @@ moe_status check_desc(const moe_desc* d) {
 // Variant for one GEMM: the direct-to-LDS kernel (bf16 or fp32) when K fills
 // whole 128-byte stages and byte offsets fit in 32 bits; its row tile follows
 // the mean number of rows per expert (decode-sized segments get 32-row tiles).
+// `may_split`: the GEMM's last partial round may be cut along K.
 GemmPlan plan_gemm(const moe_desc* d, int64_t M, int64_t N, int64_t Kd, int64_t a_rows, int64_t b_expert_elems,
-                   bool dual) {
+                   bool dual, bool may_split) {
   GemmPlan p;
   // whole 128-byte K stages and 32-bit byte offsets
   const int eb = elem_bytes(d->dtype);
@@ -81,9 +82,29 @@ GemmPlan plan_gemm(const moe_desc* d, int64_t M, int64_t N, int64_t Kd, int64_t 
   if (direct_ok) {
     const int64_t mean = M / d->E;
     p.var = mean >= 512 ? VAR_BF16_M256 : (mean >= 64 ? VAR_BF16_M128 : VAR_BF16_M32);
-    // decode-sized bf16 segments: the weight-streaming kernel, which reads
-    // every weight row in 1 KB runs
-    if (p.var == VAR_BF16_M32 && d->dtype == MOE_BF16 && Kd % kStreamChunk == 0 && N % 32 == 0) p.var = VAR_BF16_S32;
+    // Decode-sized bf16 segments: the weight-streaming kernel, which reads
+    // every weight row in 1 KB runs.  Its wide tiles (256 weight rows) have
+    // their last partial round split along K, which costs a fix-up launch;
+    // its narrow tiles (128 weight rows) never split.  The narrow ones are
+    // taken when their estimated makespan, in wide-tile times over rounds of
+    // kSplitMaxCU blocks, is no longer (min(E, M) experts with rows, each with
+    // ceil(mean / 32) row tiles, at least one, times the column tiles) --
+    // except that split wide tiles are kept when the narrow ones would fill
+    // a single round: on the 64-token Mixtral-shaped down projection (256
+    // narrow tiles, or 128 wide ones in two K parts) the split wide tiles
+    // measured 15 us faster, fix-up included, while on its gate_up GEMM
+    // (1792 narrow tiles, 7 rounds) the narrow ones saved 5 us.
+    if (p.var == VAR_BF16_M32 && d->dtype == MOE_BF16 && Kd % kStreamChunk == 0 && N % 32 == 0) {
+      const int64_t act = M < d->E ? M : d->E;
+      const int64_t rt = mean > 32 ? (mean + 31) / 32 : 1;
+      const int64_t c8 = dual ? 128 : 256;
+      const int64_t n8 = act * rt * ((N + c8 - 1) / c8), n4 = act * rt * ((N + c8 / 2 - 1) / (c8 / 2));
+      const bool split8 = may_split && Kd / kStreamChunk >= kMaxSplitParts;
+      const auto clamp = [](int64_t v) { return (int)(v < INT_MAX / 2 ? v : INT_MAX / 2); };
+      const float e8 = est_rounds(clamp(n8), kSplitMaxCU, split8 ? kSplitMaxCU : 0);
+      const float e4 = est_rounds(clamp(n4), kSplitMaxCU, 0) / 2;
+      p.var = e4 <= e8 && !(split8 && n4 <= kSplitMaxCU) ? VAR_BF16_S32N : VAR_BF16_S32;
+    }
   } else {
     // Generic kernel: 64-row tiles when 128-row ones would not fill two
     // rounds of a 256-CU part (a fixed count, so the workspace size does not
@@ -109,8 +130,8 @@ Layout layout_of(const moe_desc* d) {
   const int64_t G = swiglu ? 2 : 1;
   L.M = M;
   L.nchunks = (int32_t)((M + kDispatchChunk - 1) / kDispatchChunk);
-  L.g1 = plan_gemm(d, M, F, D, T, G * F * D, swiglu);
-  L.g2 = plan_gemm(d, M, D, F, M, D * F, false);
+  L.g1 = plan_gemm(d, M, F, D, T, G * F * D, swiglu, true);
+  L.g2 = plan_gemm(d, M, D, F, M, D * F, false, d->deterministic != 0);
   // With 256- or 32-row tiles, a GEMM's items past its last full round of CUs
   // are cut along K (fp32 partial tiles, reduced in part order by a fix-up
   // kernel that then applies the epilogue) so they fill one round of shorter
@@ -122,6 +143,7 @@ Layout layout_of(const moe_desc* d) {
   // (the tiny fp32 block has 2 K steps per GEMM).
   const int eb = elem_bytes(d->dtype);
   auto splits = [&](int var, int64_t Kd) {
+    if (var == VAR_BF16_S32N) return false;
     if (var == VAR_BF16_S32) return Kd / kStreamChunk >= kMaxSplitParts;  // K steps of 512
     return (var == VAR_BF16_M256 || var == VAR_BF16_M32) && Kd * eb / 128 >= kMaxSplitParts;
   };

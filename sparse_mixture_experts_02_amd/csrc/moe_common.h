@@ -167,7 +167,8 @@ enum Variant {
   VAR_BF16_M128 = 2,
   VAR_BF16_M32 = 3,
   VAR_GENERIC_M64 = 4,
-  VAR_BF16_S32 = 5,  // weight-streaming 32-row tiles (gemm_stream.hip): bf16, K a multiple of 512
+  VAR_BF16_S32 = 5,   // weight-streaming 32-row tiles of 256 weight rows (gemm_stream.hip)
+  VAR_BF16_S32N = 6,  // the same with 128 weight rows per tile, never split along K
 };
 int variant_rows(int var);
 int variant_cols(int var, bool dual);
@@ -212,9 +213,10 @@ constexpr int kSplitTileCols = 256;  // columns of a partial tile (rows: GemmArg
 hipError_t launch_split_fixup(int dtype, int epi, const GemmArgs& a, int32_t ncu, hipStream_t s);
 // The direct-to-LDS variants (VAR_BF16_*) for dtype 1 (bf16) or 0 (fp32).
 hipError_t launch_gemm_bf16(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s);
-// The weight-streaming variant (VAR_BF16_S32, bf16 only).
+// The weight-streaming variants (bf16 only): `strips` = 8 (VAR_BF16_S32) or
+// 4 (VAR_BF16_S32N) strips of 32 weight rows per tile.
 constexpr int kStreamChunk = 512;  // K elements per chunk of the weight-streaming kernel
-hipError_t launch_gemm_stream(int epi, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_stream(int epi, int strips, const GemmArgs& a, hipStream_t s);
 
 struct FinalizeArgs {
   const float* src;   // slot rows (T*K, D) when K > 0 slots, or (T, D) accumulation

@@ -227,12 +227,20 @@ def test_noalloc_refuses_oversize_before_any_launch(lib):
 @pytest.mark.parametrize("kw,g1,g2", [
     # the Mixtral-shaped prefill: 2048 rows per expert -> 256-row tiles with tail strips
     (dict(T=8192, D=4096, F=14336, E=8, K=2, dtype=1), "direct_m256_tail", "direct_m256_tail"),
-    # the 64-token decode batch: 16 rows per expert, bf16, K a multiple of 512 -> weight streaming
-    (dict(T=64, D=4096, F=14336, E=8, K=2, dtype=1), "stream_m32", "stream_m32"),
+    # the 64-token decode batch: 16 rows per expert, bf16, K a multiple of 512 -> weight streaming:
+    # gate_up on narrow tiles (1792 items, 7 whole rounds of 256 CUs, no K split needed); the down
+    # GEMM's 256 narrow items would fill one round, so in the deterministic mode it takes 128 wide
+    # tiles cut in two along K (the atomic combine never splits: narrow tiles)
+    (dict(T=64, D=4096, F=14336, E=8, K=2, dtype=1), "stream_m32_narrow", "stream_m32_narrow"),
+    (dict(T=64, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=1), "stream_m32_narrow", "stream_m32"),
+    # one token: 2 experts x 16 down column tiles of 256 -> wide tiles cut in 8 along K
+    # (deterministic mode only; the atomic combine never splits)
+    (dict(T=1, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=1), "stream_m32_narrow", "stream_m32"),
+    (dict(T=1, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=0), "stream_m32_narrow", "stream_m32_narrow"),
     # the same in fp32: the direct 32-row tiles
     (dict(T=64, D=4096, F=14336, E=8, K=2, dtype=0), "direct_m32", "direct_m32"),
     # gate_up contracts over D = 768 (not a multiple of 512), down over F = 1024
-    (dict(T=64, D=768, F=1024, E=8, K=2, dtype=1), "direct_m32", "stream_m32"),
+    (dict(T=64, D=768, F=1024, E=8, K=2, dtype=1), "direct_m32", "stream_m32_narrow"),
     # gate_up's 1040 output columns are a multiple of 16 but not of 32; down
     # contracts over 1040 (not whole 128-byte stages) -> the generic kernel
     (dict(T=64, D=1024, F=1040, E=8, K=2, dtype=1), "direct_m32", "generic_m64"),
@@ -253,14 +261,21 @@ def test_gemm_plan_picks_the_kernel_for_the_shape(lib, kw, g1, g2):
 
 
 def test_gemm_plan_k_split_rules(lib):
-    # decode: both streaming GEMMs have >= 8 chunks of 512 along K; the down
-    # GEMM splits only in the deterministic mode
-    det = moe.moe_gemm_plan(_desc(T=64, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=1))
-    atom = moe.moe_gemm_plan(_desc(T=64, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=0))
-    assert det["gate_up"]["k_split"] and det["down"]["k_split"]
-    assert atom["gate_up"]["k_split"] and not atom["down"]["k_split"]
-    # a 3584-long contraction has 7 chunks of 512: no split of the streaming GEMM
-    short = moe.moe_gemm_plan(_desc(T=64, D=3584, F=14336, E=8, K=2, dtype=1, deterministic=1))
-    assert short["gate_up"]["variant"] == "stream_m32" and not short["gate_up"]["k_split"]
+    # wide streaming tiles: 4 experts x 8 gate_up column tiles = 32 items, cut
+    # into 8 K parts (8 chunks of 512 each); the narrow tiles would fill only
+    # 64 of 256 CUs
+    p = moe.moe_gemm_plan(_desc(T=16, D=4096, F=1024, E=4, K=2, dtype=1, deterministic=1))
+    assert p["gate_up"]["variant"] == "stream_m32" and p["gate_up"]["k_split"]
+    # the down GEMM splits only in the deterministic mode
+    det = moe.moe_gemm_plan(_desc(T=1, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=1))
+    atom = moe.moe_gemm_plan(_desc(T=1, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=0))
+    assert det["down"]["k_split"] and not atom["down"]["k_split"]
+    # a 3584-long contraction has 7 chunks of 512: never split -> narrow tiles
+    short = moe.moe_gemm_plan(_desc(T=16, D=3584, F=1024, E=4, K=2, dtype=1, deterministic=1))
+    assert short["gate_up"]["variant"] == "stream_m32_narrow" and not short["gate_up"]["k_split"]
+    # the narrow tiles never split
+    for q in (det, atom, short):
+        for g in ("gate_up", "down"):
+            assert not (q[g]["variant"] == "stream_m32_narrow" and q[g]["k_split"])
     with pytest.raises(ValueError):
         moe.moe_gemm_plan(_desc(K=0))

@@ -139,15 +139,19 @@ EDGE_LAST = [
 
 # Decode-sized bf16 segments with K a multiple of 512 take the weight-streaming
 # kernel: 1 to 16 K chunks of 512 (odd and even counts, so both ways through
-# its two-chunk loop), K-split parts of two chunks, the ReLU (256-column) and
-# SwiGLU (128-column) tiles, a column tail off the tile width, experts with
-# more than 32 rows.  The last field names the kernels the plan must pick.
+# its two-chunk loop), the narrow (128 weight rows) and wide (256, with its
+# last round split along K: parts of one and two chunks) tiles, the ReLU and
+# SwiGLU epilogues, a column tail off the tile width, experts with more than
+# 32 rows.  The last field names the kernels the plan must pick (gate_up,
+# down) in the atomic and in the deterministic mode.
+S, SN, M32, G64 = "stream_m32", "stream_m32_narrow", "direct_m32", "generic_m64"
 STREAM = [
-    (40, 1024, 1536, 8, 2, "swiglu", "bf16", False, True, ("stream_m32", "stream_m32")),
-    (24, 1536, 2048, 4, 2, "relu", "bf16", True, True, ("stream_m32", "stream_m32")),
-    (16, 8192, 512, 4, 2, "swiglu", "bf16", False, True, ("stream_m32", "stream_m32")),
-    (30, 512, 1056, 8, 2, "swiglu", "bf16", True, False, ("stream_m32", "generic_m64")),
-    (50, 2560, 512, 8, 3, "relu", "bf16", False, True, ("stream_m32", "stream_m32")),
+    (40, 1024, 1536, 8, 2, "swiglu", "bf16", False, True, {False: (SN, SN), True: (SN, SN)}),
+    (24, 1536, 2048, 4, 2, "relu", "bf16", True, True, {False: (SN, SN), True: (SN, SN)}),
+    (16, 8192, 512, 4, 2, "swiglu", "bf16", False, True, {False: (S, SN), True: (S, SN)}),
+    (30, 512, 1056, 8, 2, "swiglu", "bf16", True, False, {False: (SN, G64), True: (SN, G64)}),
+    (50, 2560, 512, 8, 3, "relu", "bf16", False, True, {False: (SN, SN), True: (SN, SN)}),
+    (3, 512, 4096, 4, 2, "relu", "bf16", True, True, {False: (SN, SN), True: (SN, S)}),
 ]
 
 
@@ -158,7 +162,7 @@ def test_weight_streaming_shapes(case, det):
     desc = moe.make_desc(T, D, F, E, K, norm_topk_prob=norm, act="silu" if act == "swiglu" else "relu",
                          dtype=torch.bfloat16, deterministic=det)
     plan = moe.moe_gemm_plan(desc)
-    assert (plan["gate_up"]["variant"], plan["down"]["variant"]) == kernels, plan
+    assert (plan["gate_up"]["variant"], plan["down"]["variant"]) == kernels[det], plan
     cfg = workloads.small_config(T, D, F, E, K, act=act, dtype=dt, norm=norm, biases=biases,
                                  router_bias="zipf" if E >= 8 else None, cfg_id=500 + E + K)
     inp = workloads.generate(cfg)
