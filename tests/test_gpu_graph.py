@@ -101,12 +101,18 @@ def _replay_matches_eager(inp, noalloc, n_replays=4):
 
 
 @pytest.mark.parametrize("noalloc", [False, True])
-@pytest.mark.parametrize("name_or_cfg", ["tiny", "relu_small", "bf16_small"])
+@pytest.mark.parametrize("name_or_cfg", ["tiny", "relu_small", "bf16_small", "bf16_decode", "bf16_stream_split"])
 def test_graph_replay_matches_eager(name_or_cfg, noalloc):
     if name_or_cfg == "relu_small":
         name_or_cfg = workloads.small_config(700, 256, 512, 8, 2, act="relu", dtype="f32", biases=True, cfg_id=980)
     elif name_or_cfg == "bf16_small":
         name_or_cfg = workloads.small_config(1000, 512, 768, 16, 4, dtype="bf16", router_bias="zipf", cfg_id=981)
+    elif name_or_cfg == "bf16_decode":
+        # decode-sized segments: both GEMMs on the narrow weight-streaming tiles
+        name_or_cfg = workloads.small_config(48, 1024, 1536, 8, 2, dtype="bf16", router_bias="zipf", cfg_id=982)
+    elif name_or_cfg == "bf16_stream_split":
+        # three tokens, F = 4096: the down GEMM on wide streaming tiles cut along K, then the fix-up
+        name_or_cfg = workloads.small_config(3, 512, 4096, 4, 2, act="relu", dtype="bf16", biases=True, cfg_id=983)
     inp = workloads.generate(name_or_cfg)
     _say("graph %s noalloc=%s" % (inp["cfg"].get("desc", inp["cfg"]), noalloc))
     _replay_matches_eager(inp, noalloc)
