@@ -304,6 +304,31 @@ def test_capacity_dispatch_order_is_exact():
     np.testing.assert_array_equal(r["sorted_token"].cpu().numpy()[:n], order // K)
 
 
+# ------------------------------------------------ small and ragged batches
+@pytest.mark.parametrize("T,E,K,dtype", [(1, 8, 2, "f32"), (17, 16, 4, "bf16"), (40, 8, 2, "bf16"),
+                                         (63, 16, 3, "f32"), (64, 16, 16, "bf16")])
+def test_small_batches_with_routing_options(T, E, K, dtype):
+    """Decode-sized batches (one token; router blocks of 16 tokens with a
+    ragged last block; K = E) through the one-block sort, with replay of a
+    masked record, the dynamic threshold and the per-block statistics."""
+    inp = _cfg(T, 64, 96, E, K, dtype=dtype, cfg_id=290 + T)
+    rng = np.random.default_rng(T)
+    record = np.stack([rng.choice(E, K, replace=False) for _ in range(T)])
+    mask = rng.random(T) < 0.5
+    _say("fused route+sort T=%d E=%d K=%d %s" % (T, E, K, dtype))
+    g = run_gpu(inp, replay=record, replay_mask=mask)
+    ref, _ = reference(inp, g, replay=record, replay_mask=mask)
+    compare(inp, g, ref)
+    compare_stats(inp, g, ref)
+    np.testing.assert_array_equal(g["sel"][mask], record[mask])
+    np.testing.assert_array_equal(g["counts"], np.bincount(g["sel"].ravel(), minlength=E))
+    thr = safe_threshold(inp, 0.5)
+    g2 = run_gpu(inp, dynamic_threshold=thr)
+    ref2, _ = reference(inp, g2, threshold=thr)
+    compare(inp, g2, ref2)
+    compare_stats(inp, g2, ref2)
+
+
 # ------------------------------------------------------------- statistics
 @pytest.mark.parametrize("name_or_cfg", ["tiny", "relu"])
 def test_stats_plain_routing(name_or_cfg):
