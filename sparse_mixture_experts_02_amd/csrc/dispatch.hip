@@ -46,21 +46,37 @@ __global__ __launch_bounds__(kThreads) void count_kernel(DispatchArgs a) {
 }
 
 // Exclusive scan of v[0..n) (n <= kScanThreads) in LDS; returns the total.
+// Called by all kScanThreads threads; thread i reads and writes only v[i].
+// Each wave scans its 64 values with shuffles, wave 0 scans the wave totals,
+// and each value adds its wave's offset: three barriers whatever n is.
 __device__ int block_exclusive_scan(int* v, int* tmp, int n) {
-  const int tid = threadIdx.x;
-  int x = tid < n ? v[tid] : 0;
-  tmp[tid] = x;
-  __syncthreads();
-  for (int off = 1; off < n; off <<= 1) {
-    int y = (tid >= off && tid < n) ? tmp[tid - off] : 0;
-    __syncthreads();
-    if (tid < n) tmp[tid] += y;
-    __syncthreads();
+  constexpr int NWV = kScanThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int x = tid < n ? v[tid] : 0;
+  int s = x;  // inclusive scan inside the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(s, off);
+    if (lane >= off) s += y;
   }
-  const int total = n > 0 ? tmp[n - 1] : 0;
-  if (tid < n) v[tid] = tmp[tid] - x;
+  if (lane == 63) tmp[wv] = s;
   __syncthreads();
-  return total;
+  if (wv == 0) {
+    const int t = lane < NWV ? tmp[lane] : 0;
+    int u = t;
+#pragma unroll
+    for (int off = 1; off < NWV; off <<= 1) {
+      const int y = __shfl_up(u, off);
+      if (lane >= off) u += y;
+    }
+    if (lane < NWV) tmp[NWV + lane] = u - t;  // exclusive offset of wave `lane`
+  }
+  __syncthreads();
+  const int excl = s - x + tmp[NWV + wv];
+  if (tid < n) v[tid] = excl;
+  if (tid == n - 1) tmp[2 * NWV] = excl + x;
+  __syncthreads();
+  return n > 0 ? tmp[2 * NWV] : 0;
 }
 
 // Work lists of the grouped GEMMs from the per-expert counts `cnts` and
