@@ -26,7 +26,7 @@ extern "C" {
  *   <= 0 or out is NULL.
  * moe_probe_mfma_flops: the FLOPs one such launch performs (0 for bad sizes).
  * moe_probe_read: `blocks` blocks of 256 threads read `bytes` bytes of the
- *   device buffer `buf` once, in 16-byte loads, grid-stride.  out: device
+ *   device buffer `buf` once, in 16-byte non-temporal loads, grid-stride.  out: device
  *   fp32, blocks * 256 elements.  MOE_EINVAL if a pointer is NULL, buf is not
  *   16-byte aligned, bytes <= 0 or not a multiple of 16, or blocks <= 0. */
 moe_status moe_probe_mfma(int32_t blocks, int32_t iters, float* out, void* stream);

@@ -37,8 +37,17 @@
 namespace moe {
 namespace {
 
-__device__ __forceinline__ void lds_dma16(const char* src, char* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+// Cache policy of the weight loads: each weight byte is read once per layer
+// call, so the loads carry the non-temporal hint (the NT bit of gfx950's
+// cache-policy field) and do not displace the activation rows and the rest
+// of the caches' contents.  Measured on the 64-token Mixtral-shaped layer:
+// gate_up 0.310 -> 0.297 ms, down 0.168 -> 0.146 ms.  (On the prefill GEMM,
+// whose operands are re-read from L2 by neighbouring tiles, the same hint
+// costs 7-50%.)
+constexpr int kWeightCachePolicy = 2;
+
+__device__ __forceinline__ void lds_dma16_stream(const char* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kWeightCachePolicy);
 }
 
 // Wait until at most N vector-memory loads of this wave are in flight and
@@ -147,7 +156,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     const char* src = Bbase + strip_row(j) * ldb_b + (int64_t)(c0 + st / NS) * kRowB;
     char* dst = bbuf + buf * kStageB;
 #pragma unroll
-    for (int q = 0; q < kLoads; ++q) lds_dma16(src + boff[q], dst + (8 * w + q) * kRowB);
+    for (int q = 0; q < kLoads; ++q) lds_dma16_stream(src + boff[q], dst + (8 * w + q) * kRowB);
   };
   // weight fragment of slice s: row l32, logical chunk 16w + 2s + h
   auto frag = [&](const char* buf, int s) {

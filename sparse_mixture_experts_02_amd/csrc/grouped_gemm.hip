@@ -222,7 +222,9 @@ hipError_t launch_tag(int epi, const GemmArgs& a, hipStream_t s) {
 }
 
 // out[t, :] = sum over k ascending of src[t*K + k, :] (K = 1: a copy or
-// cast), four columns per thread when the rows are 16-byte aligned.
+// cast), four columns per thread when the rows are 16-byte aligned.  The
+// slot rows are read once, with the non-temporal hint (the 128-expert
+// layer's 1.07 GB of slot rows: 0.253 -> 0.208 ms).
 __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
   const int64_t D = a.D;
   if ((D & 3) == 0) {
@@ -232,11 +234,11 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
       float4 s = {0.f, 0.f, 0.f, 0.f};
       for (int k = 0; k < a.K; ++k) {
         if (a.slot_expert && a.slot_expert[t * a.K + k] >= a.E) continue;
-        const float4 v = *reinterpret_cast<const float4*>(a.src + (t * a.K + k) * D + d);
-        s.x += v.x;
-        s.y += v.y;
-        s.z += v.z;
-        s.w += v.w;
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.src + (t * a.K + k) * D + d));
+        s.x += v[0];
+        s.y += v[1];
+        s.z += v[2];
+        s.w += v[3];
       }
       if (a.out_bf16) {
         uint2 pk;
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
     const int64_t t = idx / D, d = idx - t * D;
     float s = 0.f;
     for (int k = 0; k < a.K; ++k)
-      if (!a.slot_expert || a.slot_expert[t * a.K + k] < a.E) s += a.src[(t * a.K + k) * D + d];
+      if (!a.slot_expert || a.slot_expert[t * a.K + k] < a.E) s += __builtin_nontemporal_load(a.src + (t * a.K + k) * D + d);
     if (a.out_bf16)
       static_cast<uint16_t*>(a.out)[idx] = (uint16_t)f32_to_bf16_bits(s);
     else
