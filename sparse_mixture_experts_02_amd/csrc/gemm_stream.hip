@@ -9,8 +9,9 @@
 // (SwiGLU: NS/2 gate strips and the matching up strips -> 16*NS h columns).
 // The wide tile (NS = 8) has the shape of gemm_bf16.hip's 32-row tile, with
 // its work lists and K split; the narrow one (NS = 4) has twice the column
-// tiles and never splits (the host takes it when its items fill whole rounds
-// of the CUs, so that no fix-up kernel is needed).  What differs from
+// tiles and never splits (the host plan picks between them from the
+// estimated makespan, so that a GEMM whose narrow items fill whole rounds of
+// the CUs needs no fix-up kernel).  What differs from
 // gemm_bf16.hip is the order in which the weights are read.  HBM serves a
 // weight tile read as 32 rows x 1 KB per step about a fifth faster than as
 // 256 rows x 128 bytes per step (a read probe over the Mixtral-shaped gate_up
@@ -21,7 +22,8 @@
 // hold partial sums for all NS strips; they meet once, in LDS, at the end of
 // the tile, summed in wave order (reproducible).  The activation rows go
 // straight to registers as MFMA fragments (they are small and every tile of
-// an expert reads the same rows, so they come from L2).
+// an expert reads the same rows, so they come from L2); the weights, read
+// once, go around the caches (non-temporal loads, below).
 //
 // LDS: five weight stages of 32 KB; rows are 1 KB with the 16-byte chunk
 // index XOR-ed with the row's low four bits, so the 32 rows of a fragment read
