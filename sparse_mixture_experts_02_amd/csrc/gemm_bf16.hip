@@ -539,20 +539,22 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(GemmArgs a) {
   constexpr int C4 = OUTC / 4;
   for (int idx = m0 * C4 + (int)threadIdx.x; idx < m1 * C4; idx += 256) {
     const int m = idx / C4, c = (idx - m * C4) * 4;
+    // all parts' loads first (one memory round trip, not P); parts past P
+    // re-read the last one and are not added
+    f32x4 v[kMaxSplitParts], u[kMaxSplitParts];
+#pragma unroll
+    for (int p = 0; p < kMaxSplitParts; ++p) {
+      const int pp = p < P ? p : P - 1;
+      const float* src = a.partial + ((int64_t)(j * P + pp) * a.split_rows + m) * kSplitTileCols + c;
+      v[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src));
+      if constexpr (DUAL) u[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + OUTC));
+    }
     f32x4 s0{0.f, 0.f, 0.f, 0.f}, s1{0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < P; ++p) {
-      const float* src = a.partial + ((int64_t)(j * P + p) * a.split_rows + m) * kSplitTileCols + c;
-      const float4 v = *reinterpret_cast<const float4*>(src);
-      s0[0] += v.x;
-      s0[1] += v.y;
-      s0[2] += v.z;
-      s0[3] += v.w;
-      if constexpr (DUAL) {
-        const float4 u = *reinterpret_cast<const float4*>(src + OUTC);
-        s1[0] += u.x;
-        s1[1] += u.y;
-        s1[2] += u.z;
-        s1[3] += u.w;
+#pragma unroll
+    for (int p = 0; p < kMaxSplitParts; ++p) {
+      if (p < P) {
+        s0 += v[p];
+        if constexpr (DUAL) s1 += u[p];
       }
     }
     const RowCtx rc = row_ctx<EPI>(a, r0 + m);
