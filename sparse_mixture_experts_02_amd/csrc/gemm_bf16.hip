@@ -6,9 +6,10 @@
 //
 // Tile: BM sorted rows x 256 weight rows (SwiGLU: 128 gate + the 128 matching
 // up rows, so 128 h columns; otherwise 256 output columns).  MFMA
-// v_mfma_f32_32x32x16_bf16 (fp32: four v_mfma_f32_32x32x2f32 per 16-byte
-// fragment) with the weights as operand 0, so a lane's accumulators are
-// groups of four consecutive output columns of one row.
+// v_mfma_f32_32x32x16_bf16 (the bf16 256-row tile: v_mfma_f32_16x16x32_bf16;
+// fp32: four v_mfma_f32_32x32x2f32 per 16-byte fragment) with the weights as
+// operand 0, so a lane's accumulators are groups of four consecutive output
+// columns of one row.
 // The 256-row tile runs 8 waves (two per SIMD) as a 4 x 2 grid of 64 x 128
 // wave tiles and can take an expert's tail of up to kTailRows more rows; the
 // 128-row tile runs 4 waves (2 x 2); the decode tile (BM 32) runs 4 waves
@@ -226,19 +227,40 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   // tile, lane l holds output row (token) l%32 and columns 8q + 4(l/32) + r,
   // q, r = 0..3 (accumulator element 4q + r).  Each operand fragment is 16
   // bytes per lane: row l%32, k = 8(l/32)..+8 of a 16-k slice.
-  f32x16 acc[NACC][SM][SN];
+  // The bf16 ping-pong tile runs v_mfma_f32_16x16x32_bf16 instead (M16): on
+  // this part, with the clock under the power cap, back-to-back 16x16x32
+  // MFMAs sustain about a fifth more FLOP/s than 32x32x16 ones (probe: 2.31
+  // against 1.90 PFLOP/s at two waves per SIMD), for the same LDS fragment
+  // bytes and accumulator registers per wave.  Its 16x16 blocks: lane l
+  // holds row l%16 of a block and, as an operand, the 8 k of chunk l/16 of a
+  // 32-k half stage; its accumulator holds 4 consecutive output columns
+  // 4(l/16).. of row l%16 (the same pairing of k in both operands, and the
+  // same fp32 sums as the 32x32 blocks: results are bitwise identical).
+  constexpr bool M16 = PP && EB == 2;
+  constexpr int FE = M16 ? 16 : 32;            // MFMA block edge
+  constexpr int SMb = WM / FE, SNb = WN / FE;  // row blocks per wave, column blocks per half
+  using accT = std::conditional_t<M16, f32x4, f32x16>;
+  accT acc[NACC][SMb][SNb];
 #pragma unroll
   for (int q = 0; q < NACC; ++q)
 #pragma unroll
-    for (int mi = 0; mi < SM; ++mi)
+    for (int mi = 0; mi < SMb; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < SN; ++ni) acc[q][mi][ni] = f32x16{};
-  // Tail strip g (rows BM + 32g .. +32) of wave group g: two 32x32 blocks per
-  // wave.  With wg = wm - 2g (0 or 1): SwiGLU, the gate and up blocks of h
-  // columns wn*WN + 32*wg ..; otherwise output column blocks 2*wg and
-  // 2*wg + 1 of the wave's WN columns.  Both use B fragments the wave
-  // already holds.
-  f32x16 accx[2] = {f32x16{}, f32x16{}};
+      for (int ni = 0; ni < SNb; ++ni) acc[q][mi][ni] = accT{};
+  // Tail strip g (rows BM + 32g .. +32) of wave group g, with wg = wm - 2g
+  // (0 or 1).  32x32 blocks: two per wave, SwiGLU the gate and up blocks of
+  // h columns wn*WN + 32*wg ..; otherwise output column blocks 2*wg and
+  // 2*wg + 1 of the wave's WN columns.  16x16 blocks: the strip's 16-row
+  // block wg times all of the wave's columns.  Both use B fragments the
+  // wave already holds.
+  constexpr int NX = M16 ? NACC * SNb : 2;
+  accT accx[NX];
+#pragma unroll
+  for (int i = 0; i < NX; ++i) accx[i] = accT{};
+  const int l16 = lane & 15, h16 = lane >> 4;
+  int co16[2];  // 32-k half stage hs is chunks 4hs .. 4hs+3
+#pragma unroll
+  for (int t = 0; t < 2; ++t) co16[t] = ((4 * t + h16) ^ swz(l16)) * 16;
 
   const int l32 = lane & 31, h = lane >> 5;
   // Fragment addresses (bytes inside a stage): row*KB + swizzled chunk; the
@@ -263,8 +285,8 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   if constexpr (S == 2 && NW == 8 && NT == 4) {
     // Ping-pong schedule of the 8-wave tile.  Waves 0-3 (group 0) and 4-7
     // (group 1) put one wave of each group on every SIMD.  Time is cut into
-    // phases of half a stage (two 16-k slices); in every phase one group
-    // issues the 16 MFMAs of a half stage from fragments already in
+    // phases of half a stage (32 k); in every phase one group issues the
+    // MFMAs of a half stage (bf16: 32 of 16x16x32) from fragments already in
     // registers while the other group reads the fragments of its next half
     // stage from LDS (and, in its first phase of a stage, issues its loads of
     // the next stage), so the matrix core of a SIMD always has a wave with
@@ -278,14 +300,26 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // Stage k's buffer is last read in phase 3 of stage k, so the loads of
     // stage k+2 into it (issued in phase 0/1 of stage k+1) follow a barrier.
     bf16x8 fa[2][SM], fb[2][NB];
+    constexpr int GB = M16 ? NACC * SNb : 1;  // 16x16: B fragments of a half stage
+    bf16x8 ga[M16 ? SMb : 1], gb[GB], gx;
     auto memread = [&](const char* buf, int hs) {
       if (!busy) return;
+      if constexpr (M16) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+        for (int j = 0; j < GB; ++j)
+          gb[j] = *reinterpret_cast<const bf16x8*>(
+              buf + AB + ((j / SNb) * OUTC + wn * WN + (j % SNb) * 16 + l16) * KB + co16[hs]);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) fb[u][j] = rdB(buf, 2 * hs + u, j);
+        for (int mi = 0; mi < SMb; ++mi)
+          ga[mi] = *reinterpret_cast<const bf16x8*>(buf + (wm * WM + mi * 16 + l16) * KB + co16[hs]);
+      } else {
 #pragma unroll
-        for (int mi = 0; mi < SM; ++mi) fa[u][mi] = rdA(buf, 2 * hs + u, mi);
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) fb[u][j] = rdB(buf, 2 * hs + u, j);
+#pragma unroll
+          for (int mi = 0; mi < SM; ++mi) fa[u][mi] = rdA(buf, 2 * hs + u, mi);
+        }
       }
     };
     bf16x8 fx[2];
@@ -295,34 +329,56 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     auto mma = [&](auto XT_) {
       if (!busy) return;
       constexpr bool XT = XRC > 0 && decltype(XT_)::value;
-      // B fragment indices of the two tail blocks for wg = 0; wg = 1 adds DJ
-      constexpr int J0 = 0, J1 = DUAL ? SN : 1, DJ = DUAL ? 1 : 2;
-      const bool wg = wm & 1;
+      if constexpr (M16) {
+        // the tail blocks follow the row blocks, GB / SMb after each
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+        for (int mi = 0; mi < SMb; ++mi) {
 #pragma unroll
-        for (int mi = 0; mi < SM; ++mi) {
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            acc[j / SN][mi][j % SN] = mfma_frag<T>(fb[u][j], fa[u][mi], acc[j / SN][mi][j % SN]);
+          for (int j = 0; j < GB; ++j)
+            acc[j / SNb][mi][j % SNb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(gb[j], ga[mi], acc[j / SNb][mi][j % SNb], 0, 0, 0);
           if constexpr (XT) {
-            if (mi == 0) {
-              const bf16x8 b0 = wg ? fb[u][J0 + DJ] : fb[u][J0];
-              accx[0] = mfma_frag<T>(b0, fx[u], accx[0]);
-            }
-            if (mi == SM - 1) {
-              const bf16x8 b1 = wg ? fb[u][J1 + DJ] : fb[u][J1];
-              accx[1] = mfma_frag<T>(b1, fx[u], accx[1]);
+#pragma unroll
+            for (int u = 0; u < GB / SMb; ++u) {
+              const int j = mi * (GB / SMb) + u;
+              accx[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gb[j], gx, accx[j], 0, 0, 0);
             }
           }
         }
+      } else {
+        // B fragment indices of the two tail blocks for wg = 0; wg = 1 adds DJ
+        constexpr int J0 = 0, J1 = DUAL ? SN : 1, DJ = DUAL ? 1 : 2;
+        const bool wg = wm & 1;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int mi = 0; mi < SM; ++mi) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+              acc[j / SN][mi][j % SN] = mfma_frag<T>(fb[u][j], fa[u][mi], acc[j / SN][mi][j % SN]);
+            if constexpr (XT) {
+              if (mi == 0) {
+                const bf16x8 b0 = wg ? fb[u][J0 + DJ] : fb[u][J0];
+                accx[0] = mfma_frag<T>(b0, fx[u], accx[0]);
+              }
+              if (mi == SM - 1) {
+                const bf16x8 b1 = wg ? fb[u][J1 + DJ] : fb[u][J1];
+                accx[1] = mfma_frag<T>(b1, fx[u], accx[1]);
+              }
+            }
+          }
+      }
     };
     auto memread_x = [&](const char* buf, int hs, auto XT_) {
       if constexpr (XRC > 0 && decltype(XT_)::value) {
         if (!xt) return;
+        if constexpr (M16) {
+          gx = *reinterpret_cast<const bf16x8*>(buf + (BM + 32 * grp + 16 * (wm & 1) + l16) * KB + co16[hs]);
+        } else {
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          fx[u] = *reinterpret_cast<const bf16x8*>(buf + (BM + 32 * grp + l32) * KB + co[2 * hs + u]);
+          for (int u = 0; u < 2; ++u)
+            fx[u] = *reinterpret_cast<const bf16x8*>(buf + (BM + 32 * grp + l32) * KB + co[2 * hs + u]);
+        }
       }
     };
     auto phase_end = [&](bool loads) {
@@ -440,71 +496,115 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
       // raw fp32 partial sums of this K range, tile-local rows x 256 columns
       // (SwiGLU: the gate sums in columns [0,128), the up sums in [128,256))
       float* dst = a.partial + (int64_t)split_slot * a.split_rows * kSplitTileCols;
+      if constexpr (M16) {
 #pragma unroll
-      for (int mi = 0; mi < SM; ++mi) {
-        const int m = wm * WM + mi * 32 + l32;
-        if (m >= rows) continue;
+        for (int mi = 0; mi < SMb; ++mi) {
+          const int m = wm * WM + mi * 16 + l16;
+          if (m >= rows) continue;
 #pragma unroll
-        for (int q = 0; q < NACC; ++q)
-#pragma unroll
-          for (int ni = 0; ni < SN; ++ni)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              const f32x16& c0 = acc[q][mi][ni];
-              const int c = q * OUTC + wn * WN + ni * 32 + 8 * q4 + 4 * h;
-              *reinterpret_cast<float4*>(dst + m * kSplitTileCols + c) =
-                  float4{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
-            }
-      }
-      if constexpr (XRC > 0) {
-        const int m = BM + 32 * grp + l32;
+          for (int j = 0; j < NACC * SNb; ++j) {
+            const accT& c0 = acc[j / SNb][mi][j % SNb];
+            const int c = (j / SNb) * OUTC + wn * WN + (j % SNb) * 16 + 4 * h16;
+            *reinterpret_cast<float4*>(dst + m * kSplitTileCols + c) = float4{c0[0], c0[1], c0[2], c0[3]};
+          }
+        }
+        const int m = BM + 32 * grp + 16 * (wm & 1) + l16;
         if (xw && m < rows) {
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              const f32x16& c0 = accx[i];
-              const int c = (DUAL ? i * OUTC : 0) + xcol(i) + 8 * q4 + 4 * h;
-              *reinterpret_cast<float4*>(dst + m * kSplitTileCols + c) =
-                  float4{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
-            }
+          for (int j = 0; j < NX; ++j) {
+            const accT& c0 = accx[j];
+            const int c = (j / SNb) * OUTC + wn * WN + (j % SNb) * 16 + 4 * h16;
+            *reinterpret_cast<float4*>(dst + m * kSplitTileCols + c) = float4{c0[0], c0[1], c0[2], c0[3]};
+          }
         }
+        return;
+      } else {
+#pragma unroll
+        for (int mi = 0; mi < SM; ++mi) {
+          const int m = wm * WM + mi * 32 + l32;
+          if (m >= rows) continue;
+#pragma unroll
+          for (int q = 0; q < NACC; ++q)
+#pragma unroll
+            for (int ni = 0; ni < SN; ++ni)
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x16& c0 = acc[q][mi][ni];
+                const int c = q * OUTC + wn * WN + ni * 32 + 8 * q4 + 4 * h;
+                *reinterpret_cast<float4*>(dst + m * kSplitTileCols + c) =
+                    float4{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
+              }
+        }
+        if constexpr (XRC > 0) {
+          const int m = BM + 32 * grp + l32;
+          if (xw && m < rows) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x16& c0 = accx[i];
+                const int c = (DUAL ? i * OUTC : 0) + xcol(i) + 8 * q4 + 4 * h;
+                *reinterpret_cast<float4*>(dst + m * kSplitTileCols + c) =
+                    float4{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
+              }
+          }
+        }
+        return;
       }
-      return;
     }
   }
 
   const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;
+  if constexpr (M16) {
 #pragma unroll
-  for (int mi = 0; mi < SM; ++mi) {
-    const int m = wm * WM + mi * 32 + l32;
-    if (m >= rows) continue;
-    const RowCtx rc = row_ctx<EPI>(a, r0 + m);
+    for (int mi = 0; mi < SMb; ++mi) {
+      const int m = wm * WM + mi * 16 + l16;
+      if (m >= rows) continue;
+      const RowCtx rc = row_ctx<EPI>(a, r0 + m);
 #pragma unroll
-    for (int ni = 0; ni < SN; ++ni)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x16& c0 = acc[0][mi][ni];
-        const f32x16& c1 = acc[NACC - 1][mi][ni];
-        const f32x4 v0{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
-        const f32x4 v1{c1[4 * q4], c1[4 * q4 + 1], c1[4 * q4 + 2], c1[4 * q4 + 3]};
-        epilogue4<elem, EPI>(a, rc, n0 + wn * WN + ni * 32 + 8 * q4 + 4 * h, v0, v1, bias);
-      }
-  }
-  if constexpr (XRC > 0) {
-    const int m = BM + 32 * grp + l32;
+      for (int ni = 0; ni < SNb; ++ni)
+        epilogue4<elem, EPI>(a, rc, n0 + wn * WN + ni * 16 + 4 * h16, acc[0][mi][ni], acc[NACC - 1][mi][ni], bias);
+    }
+    const int m = BM + 32 * grp + 16 * (wm & 1) + l16;
     if (xw && m < rows) {
       const RowCtx rc = row_ctx<EPI>(a, r0 + m);
 #pragma unroll
-      for (int i = 0; i < (DUAL ? 1 : 2); ++i)
+      for (int ni = 0; ni < SNb; ++ni)
+        epilogue4<elem, EPI>(a, rc, n0 + wn * WN + ni * 16 + 4 * h16, accx[ni], accx[(NACC - 1) * SNb + ni], bias);
+    }
+    return;
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < SM; ++mi) {
+      const int m = wm * WM + mi * 32 + l32;
+      if (m >= rows) continue;
+      const RowCtx rc = row_ctx<EPI>(a, r0 + m);
+#pragma unroll
+      for (int ni = 0; ni < SN; ++ni)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x16& c0 = accx[i];
-          const f32x16& c1 = accx[DUAL ? 1 : i];
+          const f32x16& c0 = acc[0][mi][ni];
+          const f32x16& c1 = acc[NACC - 1][mi][ni];
           const f32x4 v0{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
           const f32x4 v1{c1[4 * q4], c1[4 * q4 + 1], c1[4 * q4 + 2], c1[4 * q4 + 3]};
-          epilogue4<elem, EPI>(a, rc, n0 + xcol(i) + 8 * q4 + 4 * h, v0, v1, bias);
+          epilogue4<elem, EPI>(a, rc, n0 + wn * WN + ni * 32 + 8 * q4 + 4 * h, v0, v1, bias);
         }
+    }
+    if constexpr (XRC > 0) {
+      const int m = BM + 32 * grp + l32;
+      if (xw && m < rows) {
+        const RowCtx rc = row_ctx<EPI>(a, r0 + m);
+#pragma unroll
+        for (int i = 0; i < (DUAL ? 1 : 2); ++i)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x16& c0 = accx[i];
+            const f32x16& c1 = accx[DUAL ? 1 : i];
+            const f32x4 v0{c0[4 * q4], c0[4 * q4 + 1], c0[4 * q4 + 2], c0[4 * q4 + 3]};
+            const f32x4 v1{c1[4 * q4], c1[4 * q4 + 1], c1[4 * q4 + 2], c1[4 * q4 + 3]};
+            epilogue4<elem, EPI>(a, rc, n0 + xcol(i) + 8 * q4 + 4 * h, v0, v1, bias);
+          }
+      }
     }
   }
 }
