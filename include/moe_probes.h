@@ -20,7 +20,7 @@ extern "C" {
 
 /*
  * moe_probe_mfma: `blocks` blocks of 8 waves, each wave issuing `iters`
- *   rounds of 8 independent v_mfma_f32_32x32x16_bf16 on register operands.
+ *   rounds of 8 independent v_mfma_f32_16x16x32_bf16 on register operands.
  *   out: device fp32, blocks * 512 elements (one word per lane, written so
  *   the work stays live; values meaningless).  MOE_EINVAL if blocks or iters
  *   <= 0 or out is NULL.

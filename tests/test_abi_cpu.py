@@ -171,8 +171,8 @@ def test_bench_refuses_several_gpus():
 
 
 def test_probes_validate_on_the_host(lib):
-    # the FLOP count of a matrix-core probe launch: 8 waves x 8 chains of 32x32x16 MFMAs per round
-    assert moe.moe_probe_mfma_flops(2, 3) == 2 * 8 * 3 * 8 * (2 * 32 * 32 * 16)
+    # the FLOP count of a matrix-core probe launch: 8 waves x 8 chains of 16x16x32 MFMAs per round
+    assert moe.moe_probe_mfma_flops(2, 3) == 2 * 8 * 3 * 8 * (2 * 16 * 16 * 32)
     assert moe.moe_probe_mfma_flops(0, 3) == 0
     einval = 1
     # rejected before any launch (no device needed)
