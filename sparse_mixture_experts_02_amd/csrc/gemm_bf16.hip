@@ -381,9 +381,15 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         }
       }
     };
-    auto phase_end = [&](bool loads) {
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's fragment reads have landed
-      if (loads) wait_vm<0>();
+    // A wave's fragment reads need to have landed before the barrier only at
+    // the end of a stage (loads into the buffer they read may follow it);
+    // elsewhere the first MFMA that uses them waits, so a reading wave does
+    // not hold up the barrier with its LDS latency (prefill gate_up -1%).
+    auto phase_end = [&](bool stage_end) {
+      if (stage_end) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's fragment reads have landed
+        wait_vm<0>();                        // and its loads of the next stage
+      }
       barrier_lds();
     };
     // The two groups run separate straight-line loops (a branch-free body
