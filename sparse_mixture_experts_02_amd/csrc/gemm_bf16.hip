@@ -385,12 +385,16 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // the end of a stage (loads into the buffer they read may follow it);
     // elsewhere the first MFMA that uses them waits, so a reading wave does
     // not hold up the barrier with its LDS latency (prefill gate_up -1%).
+    // Only the stage-end barrier orders memory; the three inside a stage
+    // keep the groups in step.  The SwiGLU tile keeps them (without them its
+    // prefill GEMM is 1% slower); the other epilogues drop them (prefill down
+    // GEMM -2.5%, the two groups then fall into step by themselves).
     auto phase_end = [&](bool stage_end) {
       if (stage_end) {
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's fragment reads have landed
         wait_vm<0>();                        // and its loads of the next stage
       }
-      barrier_lds();
+      if (DUAL || stage_end) barrier_lds();
     };
     // The two groups run separate straight-line loops (a branch-free body
     // keeps the fragments in registers); both meet the same barriers.  Each
