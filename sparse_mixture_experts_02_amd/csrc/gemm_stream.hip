@@ -122,6 +122,15 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     const int64_t src = a.a_index ? (int64_t)a.a_index[r] : (int64_t)r;
     arow = static_cast<const char*>(a.A) + src * a.lda * 2 + (16 * w + h) * 16;
   }
+  // Chunk i of this item's walk is chunk c0 + (i + rot) mod (c1 - c0): the
+  // items of an XCD start their K walks at different chunks, so at any time
+  // its CUs read different K offsets of their rows rather than the same one
+  // (the decode gate_up stream 3% faster; the sums change order only).
+  const int rot = (int)((blockIdx.x >> 3) % (unsigned)(c1 - c0));
+  auto chk = [&](int i) {
+    const int x = i + rot;
+    return c0 + (x >= c1 - c0 ? x - (c1 - c0) : x);
+  };
   auto load_a = [&](bf16x8* f, int c) {
     const char* p = arow + (int64_t)c * kRowB;
 #pragma unroll
@@ -151,11 +160,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
   for (int q = 0; q < kLoads; ++q)
     boff[q] = (uint32_t)((8 * w + q) * ldb_b) + (uint32_t)((lane ^ ((8 * w + q) & 15)) * 16);
-  // stage st (0-based in this item) = strip st % NS of chunk c0 + st / NS, in
+  // stage st (0-based in this item) = strip st % NS of chunk chk(st / NS), in
   // LDS buffer st % kStages
   auto issue_b = [&](int st, int buf) {
     const int j = st % NS;
-    const char* src = Bbase + strip_row(j) * ldb_b + (int64_t)(c0 + st / NS) * kRowB;
+    const char* src = Bbase + strip_row(j) * ldb_b + (int64_t)chk(st / NS) * kRowB;
     char* dst = bbuf + buf * kStageB;
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) lds_dma16_stream(src + boff[q], dst + (8 * w + q) * kRowB);
@@ -173,7 +182,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 
   const int nst = (c1 - c0) * NS;  // >= NS
   // Prologue: the first chunk's activations, then weight stages 0..3.
-  load_a(af, c0);
+  load_a(af, chk(0));
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t) issue_b(t, t);
   int rb = 0;  // LDS buffer of the current stage (st % kStages)
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     wait_vm<WAIT * kLoads>();
     barrier_lds();
     if constexpr (ISSUE) issue_b(st + kStages - 1, rb == 0 ? kStages - 1 : rb - 1);
-    if constexpr (NEXTA) load_a(nxt, c0 + st / NS + 1);
+    if constexpr (NEXTA) load_a(nxt, chk(st / NS + 1));
     // all eight weight fragments first: one LDS round trip per stage
     const char* buf = bbuf + rb * kStageB;
     bf16x8 bf[8];
