@@ -88,12 +88,11 @@ GemmPlan plan_gemm(const moe_desc* d, int64_t M, int64_t N, int64_t Kd, int64_t 
     // its narrow tiles (128 weight rows) never split.  The narrow ones are
     // taken when their estimated makespan, in wide-tile times over rounds of
     // kSplitMaxCU blocks, is no longer (min(E, M) experts with rows, each with
-    // ceil(mean / 32) row tiles, at least one, times the column tiles) --
-    // except that split wide tiles are kept when the narrow ones would fill
-    // a single round: on the 64-token Mixtral-shaped down projection (256
-    // narrow tiles, or 128 wide ones in two K parts) the split wide tiles
-    // measured 15 us faster, fix-up included, while on its gate_up GEMM
-    // (1792 narrow tiles, 7 rounds) the narrow ones saved 5 us.
+    // ceil(mean / 32) row tiles, at least one, times the column tiles).  On
+    // the 64-token Mixtral-shaped layer: gate_up 1792 narrow tiles in 7
+    // rounds (5 us faster than split wide tiles); down 256 narrow tiles in
+    // one round, 8 us faster than 128 wide ones in two K parts and the
+    // fix-up (15 us slower before the items' K walks were rotated).
     if (p.var == VAR_BF16_M32 && d->dtype == MOE_BF16 && Kd % kStreamChunk == 0 && N % 32 == 0) {
       const int64_t act = M < d->E ? M : d->E;
       const int64_t rt = mean > 32 ? (mean + 31) / 32 : 1;
@@ -103,7 +102,7 @@ GemmPlan plan_gemm(const moe_desc* d, int64_t M, int64_t N, int64_t Kd, int64_t 
       const auto clamp = [](int64_t v) { return (int)(v < INT_MAX / 2 ? v : INT_MAX / 2); };
       const float e8 = est_rounds(clamp(n8), kSplitMaxCU, split8 ? kSplitMaxCU : 0);
       const float e4 = est_rounds(clamp(n4), kSplitMaxCU, 0) / 2;
-      p.var = e4 <= e8 && !(split8 && n4 <= kSplitMaxCU) ? VAR_BF16_S32N : VAR_BF16_S32;
+      p.var = e4 <= e8 ? VAR_BF16_S32N : VAR_BF16_S32;
     }
   } else {
     // Generic kernel: 64-row tiles when 128-row ones would not fill two

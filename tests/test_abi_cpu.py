@@ -227,12 +227,11 @@ def test_noalloc_refuses_oversize_before_any_launch(lib):
 @pytest.mark.parametrize("kw,g1,g2", [
     # the Mixtral-shaped prefill: 2048 rows per expert -> 256-row tiles with tail strips
     (dict(T=8192, D=4096, F=14336, E=8, K=2, dtype=1), "direct_m256_tail", "direct_m256_tail"),
-    # the 64-token decode batch: 16 rows per expert, bf16, K a multiple of 512 -> weight streaming:
-    # gate_up on narrow tiles (1792 items, 7 whole rounds of 256 CUs, no K split needed); the down
-    # GEMM's 256 narrow items would fill one round, so in the deterministic mode it takes 128 wide
-    # tiles cut in two along K (the atomic combine never splits: narrow tiles)
+    # the 64-token decode batch: 16 rows per expert, bf16, K a multiple of 512 -> weight streaming
+    # on narrow tiles: gate_up 1792 items (7 whole rounds of 256 CUs), down 256 items (one round,
+    # no better than 128 wide tiles cut in two along K, so no K split and no fix-up)
     (dict(T=64, D=4096, F=14336, E=8, K=2, dtype=1), "stream_m32_narrow", "stream_m32_narrow"),
-    (dict(T=64, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=1), "stream_m32_narrow", "stream_m32"),
+    (dict(T=64, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=1), "stream_m32_narrow", "stream_m32_narrow"),
     # one token: 2 experts x 16 down column tiles of 256 -> wide tiles cut in 8 along K
     # (deterministic mode only; the atomic combine never splits)
     (dict(T=1, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=1), "stream_m32_narrow", "stream_m32"),
