@@ -95,10 +95,11 @@ using ShapeM256 = Shape<256, 8, 4, 128, 2>;  // 2 x 68 KB of LDS (with the tail 
 using ShapeM128 = Shape<128, 4, 2, 128, 2>;  // 2 x 48 KB
 using ShapeM32 = Shape<32, 4, 1, 128, 4>;    // 4 x 36 KB
 
-// EARLY_CTX: the down epilogue's row contexts (slot or token, routing
-// weight) are loaded before the K loop (bf16 256-row tile only; taken for
-// short contractions, where the epilogue weighs most).
-template <typename T, int EPI, class SH, bool EARLY_CTX = false>
+// SHORT_K: the instance of the bf16 256-row tile for short contractions (at
+// most 32 K steps), where a tile's start and end weigh most: the down
+// epilogue's row contexts (slot or token, routing weight) are loaded before
+// the K loop, and the SwiGLU tile keeps only the stage-end barriers.
+template <typename T, int EPI, class SH, bool SHORT_K = false>
 __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   using elem = typename T::elem;
   constexpr int EB = T::kBytes;
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   // row tile of an expert is usually partial) skips its MFMAs and fragment
   // reads; it still loads its share of every stage and meets every barrier.
   const bool busy = wm * WM < rows;
-  constexpr bool PFC = EARLY_CTX && M16 && (EPI == EPI_DOWN_SLOT || EPI == EPI_DOWN_ATOMIC);
+  constexpr bool PFC = SHORT_K && M16 && (EPI == EPI_DOWN_SLOT || EPI == EPI_DOWN_ATOMIC);
   RowCtx pre[PFC ? SMb + 1 : 1];
   if constexpr (PFC) {
 #pragma unroll
@@ -397,14 +398,16 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // not hold up the barrier with its LDS latency (prefill gate_up -1%).
     // Only the stage-end barrier orders memory; the three inside a stage
     // keep the groups in step.  The SwiGLU tile keeps them (without them its
-    // prefill GEMM is 1% slower); the other epilogues drop them (prefill down
-    // GEMM -2.5%, the two groups then fall into step by themselves).
+    // prefill GEMM is 1% slower, its 32-step 128-expert GEMM 1% faster: the
+    // short-contraction instance drops them); the other epilogues drop them
+    // (prefill down GEMM -2.5%, the two groups then fall into step by
+    // themselves).
     auto phase_end = [&](bool stage_end) {
       if (stage_end) {
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's fragment reads have landed
         wait_vm<0>();                        // and its loads of the next stage
       }
-      if (DUAL || stage_end) barrier_lds();
+      if ((DUAL && !SHORT_K) || stage_end) barrier_lds();
     };
     // The two groups run separate straight-line loops (a branch-free body
     // keeps the fragments in registers); both meet the same barriers.  Each
@@ -688,8 +691,9 @@ hipError_t launch_rows(int var, const GemmArgs& a, hipStream_t s) {
     case VAR_BF16_M256:
       // short contractions (at most 32 K steps of 64): the down tile loads
       // its epilogue's row contexts up front (128-expert down GEMM, 12 steps:
-      // -3.6%; over 224 steps the 14 more registers cost 1.3%)
-      if constexpr (T::kBytes == 2 && (EPI == EPI_DOWN_SLOT || EPI == EPI_DOWN_ATOMIC)) {
+      // -3.2%; over 224 steps the 14 more registers cost 1.3%), the SwiGLU
+      // tile drops its phase barriers
+      if constexpr (T::kBytes == 2 && EPI != EPI_RELU) {
         if (a.Kd <= 32 * 64) {
           hipLaunchKernelGGL((gemm_bf16_kernel<T, EPI, ShapeM256, true>), dim3(a.max_work), dim3(ShapeM256::NW * 64), 0, s,
                              a);
