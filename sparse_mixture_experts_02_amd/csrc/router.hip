@@ -106,8 +106,9 @@ __device__ __forceinline__ void logits_partial(const RouterArgs& a, int64_t t0, 
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // U k-steps per iteration: all their loads are issued before the MFMAs so
-  // several HBM round trips overlap.  Elements at or past ke read as zero.
-  constexpr int U = NT <= 2 ? 8 : (NT <= 4 ? 4 : (NT <= 8 ? 2 : 1));
+  // several HBM round trips overlap (16 for one expert tile: the 64-token
+  // decode router -2 us against 8).  Elements at or past ke read as zero.
+  constexpr int U = NT <= 1 ? 16 : NT <= 2 ? 8 : (NT <= 4 ? 4 : (NT <= 8 ? 2 : 1));
   if constexpr (sizeof(typename Tag::elem) == 2) {
     constexpr int KS = 32;
     const int64_t steps = (D + KS - 1) / KS;
