@@ -579,6 +579,35 @@ __global__ __launch_bounds__(SH::NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 
   const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;
   if constexpr (M16) {
+    // Tiles whose columns all lie inside N, without a bias, over 16-byte
+    // aligned rows (the common case) store through one row pointer per row
+    // with no per-column checks (the SwiGLU epilogue's bookkeeping otherwise
+    // costs more than its transcendentals).
+    if constexpr (EPI != EPI_DOWN_ATOMIC) {
+      using OT = std::conditional_t<EPI == EPI_DOWN_SLOT, float, elem>;
+      if (!bias && n0 + OUTC <= N && (a.ldc & 3) == 0) {
+        OT* const C = static_cast<OT*>(a.C) + n0 + wn * WN + 4 * h16;
+#pragma unroll
+        for (int mi = 0; mi < SMb; ++mi) {
+          const int m = wm * WM + mi * 16 + l16;
+          if (m >= rows) continue;
+          const RowCtx rc = PFC ? pre[mi] : row_ctx<EPI>(a, r0 + m);
+          OT* const dst = C + rc.orow * a.ldc;
+#pragma unroll
+          for (int ni = 0; ni < SNb; ++ni)
+            epilogue4_inner<OT, EPI>(dst + ni * 16, rc.wgt, acc[0][mi][ni], acc[NACC - 1][mi][ni]);
+        }
+        const int m = BM + 32 * grp + 16 * (wm & 1) + l16;
+        if (xw && m < rows) {
+          const RowCtx rc = PFC ? pre[SMb] : row_ctx<EPI>(a, r0 + m);
+          OT* const dst = C + rc.orow * a.ldc;
+#pragma unroll
+          for (int ni = 0; ni < SNb; ++ni)
+            epilogue4_inner<OT, EPI>(dst + ni * 16, rc.wgt, accx[ni], accx[(NACC - 1) * SNb + ni]);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int mi = 0; mi < SMb; ++mi) {
       const int m = wm * WM + mi * 16 + l16;

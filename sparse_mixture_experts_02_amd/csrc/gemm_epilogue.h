@@ -101,4 +101,32 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, const RowCtx& rc, i
   }
 }
 
+// The same epilogue for four columns that all lie inside N, with no bias and
+// 16-byte aligned rows (the caller checks both once per tile): no per-column
+// checks, one vector store to `dst` (the row's column nb).  SwiGLU, ReLU and
+// the slot store only (the atomic combine keeps epilogue4).
+template <typename elem, int EPI>
+__device__ __forceinline__ void epilogue4_inner(elem* dst, float wgt, const f32x4& acc0, const f32x4& acc1) {
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (EPI == EPI_SWIGLU) {
+      const float g = acc0[i], u = acc1[i];
+      v[i] = g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * g)) * u;
+    } else if constexpr (EPI == EPI_RELU) {
+      v[i] = fmaxf(acc0[i], 0.f);
+    } else {
+      v[i] = wgt * acc0[i];
+    }
+  }
+  if constexpr (sizeof(elem) == 2) {
+    uint2 pk;
+    pk.x = f32x2_to_bf16x2_bits(v[0], v[1]);
+    pk.y = f32x2_to_bf16x2_bits(v[2], v[3]);
+    *reinterpret_cast<uint2*>(dst) = pk;
+  } else {
+    *reinterpret_cast<float4*>(dst) = float4{v[0], v[1], v[2], v[3]};
+  }
+}
+
 }  // namespace moe
