@@ -110,6 +110,9 @@ EDGE = [
     (1000, 128, 320, 4, 2, "swiglu", "bf16", False, True),
     (600, 192, 448, 3, 1, "relu", "bf16", True, True),
     (4096, 128, 192, 4, 2, "swiglu", "bf16", False, True),
+    # 256-row tiles whose columns all lie inside N, without biases: the
+    # interior-tile epilogue of the ReLU and down tiles
+    (4096, 128, 256, 4, 2, "relu", "bf16", False, True),
     (40, 256, 384, 8, 2, "swiglu", "bf16", False, True),
     (64, 4096, 1024, 8, 2, "swiglu", "bf16", False, True),
     (3000, 64, 128, 40, 6, "swiglu", "bf16", False, True),
