@@ -100,16 +100,17 @@ __host__ __device__ inline int2 work_item(int L, const int* tst, const int* offs
   const int mt = tst[x + 1] - tst[x];
   const int q = L - tst[x] * ntn;
   const int full = (ntn / kColGroup) * kColGroup * mt;
+  // all operands are non-negative: unsigned division is the shorter sequence
   int m, n;
   if (q < full) {
-    const int gsz = kColGroup * mt;
-    const int grp = q / gsz, r = q - grp * gsz;
-    n = grp * kColGroup + r / mt;
-    m = r % mt;
+    const unsigned gsz = (unsigned)(kColGroup * mt);
+    const unsigned grp = (unsigned)q / gsz, r = (unsigned)q - grp * gsz;
+    n = (int)(grp * kColGroup + r / (unsigned)mt);
+    m = (int)(r % (unsigned)mt);
   } else {
-    const int r = q - full;
-    n = (ntn / kColGroup) * kColGroup + r / mt;
-    m = r % mt;
+    const unsigned r = (unsigned)(q - full);
+    n = (ntn / kColGroup) * kColGroup + (int)(r / (unsigned)mt);
+    m = (int)(r % (unsigned)mt);
   }
   // the last tile of an expert with more than bm remaining rows holds them all
   const bool tail = m == mt - 1 && offs[x + 1] - (offs[x] + m * bm) > bm;
