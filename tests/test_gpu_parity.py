@@ -202,6 +202,36 @@ def test_edge_last_expert_heavy(case, det):
     check_full_properties(inp, g)
 
 
+# 256-row tiles whose expert's last tile holds 1-64, 65-128, 129-192 and
+# 193-255 rows (so one to four of the wave row strips have rows; the waves
+# past the end skip their MFMAs): each case has last tiles in all four
+# classes (checked below) and is compared in full, in both combine modes.
+SHORT_TILES = [
+    # (T, D, F, E, K, act, biases, router bias, cfg id)
+    (4096, 128, 256, 8, 2, "swiglu", False, "zipf", 610),
+    (5000, 128, 256, 8, 2, "relu", True, None, 612),
+]
+
+
+@pytest.mark.parametrize("case", SHORT_TILES, ids=lambda c: "T%d_%s_b%d" % (c[0], c[5], c[6]))
+@pytest.mark.parametrize("det", [False, True])
+def test_short_row_tiles(case, det):
+    T, D, F, E, K, act, biases, rb, cid = case
+    desc = moe.make_desc(T, D, F, E, K, act="silu" if act == "swiglu" else "relu", dtype=torch.bfloat16,
+                         deterministic=det)
+    plan = moe.moe_gemm_plan(desc)
+    assert plan["gate_up"]["variant"] == plan["down"]["variant"] == "direct_m256_tail", plan
+    cfg = workloads.small_config(T, D, F, E, K, act=act, dtype="bf16", biases=biases, router_bias=rb, cfg_id=cid)
+    inp = workloads.generate(cfg)
+    _say("short tiles %s det=%s" % (case, det))
+    g = gpu_forward(inp, deterministic=det)
+    # last-tile rows c mod 256 above the 32 tail rows a full tile may absorb
+    classes = {(int(c) % 256 - 1) // 64 for c in g["counts"] if int(c) % 256 > 32}
+    assert classes == {0, 1, 2, 3}, g["counts"]
+    check(inp, g)
+    check_full_properties(inp, g)
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_random_small_sweep(seed):
     rng = np.random.default_rng(seed)
