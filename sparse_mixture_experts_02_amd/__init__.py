@@ -345,7 +345,9 @@ def forward(x, router, gate_up_proj, down_proj, *, top_k, norm_topk_prob=True, a
     w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
     logits = torch.empty((T, E), dtype=torch.float32, device=dev) if return_logits else None
     counts = torch.empty((E,), dtype=torch.int32, device=dev) if return_counts else None
-    if workspace is None or workspace.numel() < nbytes:
+    if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the device of x (%s), got %s" % (dev, workspace.device))
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
     biases = [None if b is None else b.to(device=dev, dtype=torch.float32).contiguous()
               for b in (router_bias, up_bias, down_bias)]

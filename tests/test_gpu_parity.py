@@ -232,6 +232,25 @@ def test_short_row_tiles(case, det):
     check_full_properties(inp, g)
 
 
+def test_caller_workspace():
+    """A caller's workspace is used when it is large enough (any dtype: its
+    size counts in bytes); one on another device is refused before a launch."""
+    inp = workloads.generate(workloads.small_config(200, 64, 128, 8, 2, dtype="bf16", cfg_id=620))
+    d = device_inputs(inp)
+    c = inp["cfg"]
+    kw = dict(top_k=c["K"], norm_topk_prob=c["norm"])
+    ref = moe.forward(d["x"], d["router"], d["gate_up"], d["down"], **kw)
+    desc = moe.make_desc(c["T"], c["D"], c["F"], c["E"], c["K"], dtype=torch.bfloat16, deterministic=True)
+    n = moe.moe_workspace_bytes(desc)
+    ws = torch.empty(((n + 3) // 4,), dtype=torch.float32, device="cuda")
+    got = moe.forward(d["x"], d["router"], d["gate_up"], d["down"], workspace=ws, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    with pytest.raises(ValueError, match="workspace"):
+        moe.forward(d["x"], d["router"], d["gate_up"], d["down"], workspace=torch.empty(n, dtype=torch.uint8), **kw)
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_random_small_sweep(seed):
     rng = np.random.default_rng(seed)
