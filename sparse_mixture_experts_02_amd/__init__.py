@@ -132,7 +132,7 @@ def moe_probe_read(buf, nbytes, blocks, out, stream) -> int:
 
 
 GEMM_VARIANTS = {0: "generic_m128", 1: "direct_m256_tail", 2: "direct_m128", 3: "direct_m32", 4: "generic_m64",
-                 5: "stream_m32", 6: "stream_m32_narrow"}
+                 5: "stream_m32", 6: "stream_m32_narrow", 7: "stream_m64_narrow"}
 
 
 def moe_gemm_plan(desc: MoeDesc) -> dict:

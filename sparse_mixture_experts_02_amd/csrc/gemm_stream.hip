@@ -73,21 +73,25 @@ constexpr int kLoads = kStrip / 4;  // load instructions per wave per stage (one
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-template <int EPI, int NS>
+// RH: 32-row halves per tile.  RH = 2 (narrow tiles only) takes 64 sorted
+// rows: each weight stage read from HBM feeds the MFMAs of both halves, so
+// an expert with 33-64 rows reads its weights once instead of twice.
+template <int EPI, int NS, int RH>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   static_assert(NS == 8 || NS == 4, "strips per tile");
+  static_assert(RH == 1 || (RH == 2 && NS == 4), "64-row tiles are narrow");
   using elem = uint16_t;
   constexpr bool DUAL = EPI == EPI_SWIGLU;
   constexpr int OUTC = DUAL ? 16 * NS : 32 * NS;  // output columns per tile
-  constexpr int BM = 32;
+  constexpr int BM = 32 * RH;
   // LDS: weight stages 0..4; reused at the end for the four waves' partial
-  // sums (4 x NS x 4 KB).
+  // sums (4 x RH x NS x 4 KB).
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageB];
   char* const bbuf = lds;
 
   if ((int)blockIdx.x >= a.num_work[0]) return;
   const int nch = (int)(a.Kd / kKC);
-  constexpr bool SPLITTABLE = EPI != EPI_DOWN_ATOMIC && NS == 8;
+  constexpr bool SPLITTABLE = EPI != EPI_DOWN_ATOMIC && NS == 8 && RH == 1;
   int2 wk = a.work[blockIdx.x];
   int c0 = 0, c1 = nch, split_slot = -1;
   if constexpr (SPLITTABLE) {
@@ -114,13 +118,15 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 
   // Activations go straight to registers as MFMA fragments: lane (l32, h)
   // of wave w holds, for 16-k slice s of the wave's quarter of a chunk, the
-  // 8 elements of sorted row l32 at chunk-local 16-byte chunk 16w + 2s + h
-  // (rows past the segment repeat its first row).
-  const char* arow;
-  {
-    const int r = r0 + (l32 < rows ? l32 : 0);
+  // 8 elements of sorted row 32hh + l32 of half hh at chunk-local 16-byte
+  // chunk 16w + 2s + h (rows past the segment repeat its first row).
+  const char* arow[RH];
+#pragma unroll
+  for (int hh = 0; hh < RH; ++hh) {
+    const int m = 32 * hh + l32;
+    const int r = r0 + (m < rows ? m : 0);
     const int64_t src = a.a_index ? (int64_t)a.a_index[r] : (int64_t)r;
-    arow = static_cast<const char*>(a.A) + src * a.lda * 2 + (16 * w + h) * 16;
+    arow[hh] = static_cast<const char*>(a.A) + src * a.lda * 2 + (16 * w + h) * 16;
   }
   // Chunk i of this item's walk is chunk c0 + (i + rot) mod (c1 - c0): the
   // items of an XCD start their K walks at different chunks, so at any time
@@ -131,10 +137,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     const int x = i + rot;
     return c0 + (x >= c1 - c0 ? x - (c1 - c0) : x);
   };
-  auto load_a = [&](bf16x8* f, int c) {
-    const char* p = arow + (int64_t)c * kRowB;
+  auto load_a = [&](bf16x8 (&f)[RH][8], int c) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) f[s] = *reinterpret_cast<const bf16x8*>(p + 32 * s);
+    for (int hh = 0; hh < RH; ++hh) {
+      const char* p = arow[hh] + (int64_t)c * kRowB;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) f[hh][s] = *reinterpret_cast<const bf16x8*>(p + 32 * s);
+    }
   };
 
   // Weights.  Wave w fills rows 8w .. 8w+7 of a 32-row stage, one 1 KB row
@@ -175,10 +184,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     return *reinterpret_cast<const bf16x8*>(buf + l32 * kRowB + ch * 16);
   };
 
-  f32x16 acc[NS];
+  f32x16 acc[RH][NS];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) acc[j] = f32x16{};
-  bf16x8 af[8], an[8];
+  for (int hh = 0; hh < RH; ++hh)
+#pragma unroll
+    for (int j = 0; j < NS; ++j) acc[hh][j] = f32x16{};
+  bf16x8 af[RH][8], an[RH][8];
 
   const int nst = (c1 - c0) * NS;  // >= NS
   // Prologue: the first chunk's activations, then weight stages 0..3.
@@ -196,7 +207,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   // copy ever waits for a load).  WAIT, in stages of kLoads loads: this
   // wave's loads issued after stage st's weights that may stay in flight
   // (the tables at `chunk`).
-  auto stage = [&](int st, bf16x8 (&cur)[8], bf16x8 (&nxt)[8], auto J_, auto ISSUE_, auto NEXTA_, auto WAIT_) {
+  auto stage = [&](int st, bf16x8 (&cur)[RH][8], bf16x8 (&nxt)[RH][8], auto J_, auto ISSUE_, auto NEXTA_,
+                   auto WAIT_) {
     constexpr int J = decltype(J_)::value, WAIT = decltype(WAIT_)::value;
     constexpr bool ISSUE = decltype(ISSUE_)::value, NEXTA = decltype(NEXTA_)::value;
     wait_vm<WAIT * kLoads>();
@@ -210,7 +222,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     for (int s = 0; s < 8; ++s) bf[s] = frag(buf, s);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) acc[J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[s], cur[s], acc[J], 0, 0, 0);
+    for (int hh = 0; hh < RH; ++hh)
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        acc[hh][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[s], cur[hh][s], acc[hh][J], 0, 0, 0);
     rb = rb == kStages - 1 ? 0 : rb + 1;
   };
   constexpr std::true_type Y{};
@@ -229,8 +244,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   //             0's weights are this chunk's own, so they have landed too);
   //             1..3: those and the activations (4).
   //   last chunk (its stages issue nothing): 3, 2, 1, 0.
+  //   With 64-row tiles the activations are 2 kLoads units (two halves), so
+  //   stages 1..3 allow 3 + 2.
   // A chunk that is not the last: every stage issues stage st+4, which exists.
-  auto chunk = [&](int st, bf16x8 (&cur)[8], bf16x8 (&nxt)[8]) {
+  auto chunk = [&](int st, bf16x8 (&cur)[RH][8], bf16x8 (&nxt)[RH][8]) {
     if constexpr (NS == 8) {
       stage(st + 0, cur, nxt, IC<0>{}, Y, Nn, IC<3>{});
       stage(st + 1, cur, nxt, IC<1>{}, Y, Y, IC<3>{});
@@ -242,12 +259,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
       stage(st + 7, cur, nxt, IC<7>{}, Y, Nn, IC<3>{});
     } else {
       stage(st + 0, cur, nxt, IC<0>{}, Y, Y, IC<3>{});
-      stage(st + 1, cur, nxt, IC<1>{}, Y, Nn, IC<4>{});
-      stage(st + 2, cur, nxt, IC<2>{}, Y, Nn, IC<4>{});
-      stage(st + 3, cur, nxt, IC<3>{}, Y, Nn, IC<4>{});
+      stage(st + 1, cur, nxt, IC<1>{}, Y, Nn, IC<3 + RH>{});
+      stage(st + 2, cur, nxt, IC<2>{}, Y, Nn, IC<3 + RH>{});
+      stage(st + 3, cur, nxt, IC<3>{}, Y, Nn, IC<3 + RH>{});
     }
   };
-  auto last_chunk = [&](int st, bf16x8 (&cur)[8], bf16x8 (&nxt)[8]) {
+  auto last_chunk = [&](int st, bf16x8 (&cur)[RH][8], bf16x8 (&nxt)[RH][8]) {
     if constexpr (NS == 8) {
       stage(st + 0, cur, nxt, IC<0>{}, Y, Nn, IC<3>{});
       stage(st + 1, cur, nxt, IC<1>{}, Y, Nn, IC<3>{});
@@ -280,77 +297,88 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   // wave is past its last fragment read once the barrier is crossed).
   __builtin_amdgcn_s_waitcnt(0xc07f);
   barrier_lds();
-  float* part = reinterpret_cast<float*>(lds);  // [wave][strip][16][64]
-  static_assert(4 * NS * 16 * 64 * 4 <= kStages * kStageB, "wave sums fit the stages");
+  float* part = reinterpret_cast<float*>(lds);  // [wave][half][strip][16][64]
+  static_assert(4 * RH * NS * 16 * 64 * 4 <= kStages * kStageB, "wave sums fit the stages");
 #pragma unroll
-  for (int j = 0; j < NS; ++j)
+  for (int hh = 0; hh < RH; ++hh)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part[((w * NS + j) * 16 + r) * 64 + lane] = acc[j][r];
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[(((w * RH + hh) * NS + j) * 16 + r) * 64 + lane] = acc[hh][j][r];
   __syncthreads();
-  auto sum4 = [&](int j) {
+  auto sum4 = [&](int hh, int j) {
     f32x16 v = f32x16{};
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] += part[((u * NS + j) * 16 + r) * 64 + lane];
+      for (int r = 0; r < 16; ++r) v[r] += part[(((u * RH + hh) * NS + j) * 16 + r) * 64 + lane];
     return v;
   };
-  // Strips each wave finishes.  SwiGLU: the gate and up strips of h columns
-  // 32i .. 32i+31 (strips i and i + NS/2) for i = w (NS = 4: waves 0 and 1
-  // only).  Otherwise strips 2w and 2w+1 (NS = 8) or strip w (NS = 4).
-  constexpr int NPW = DUAL ? 1 : NS / 4;  // output strips per wave
-  if (DUAL && w >= NS / 2) return;
-  const int ja = DUAL ? w : NPW * w;
-  const int jb = DUAL ? w + NS / 2 : NPW * w + NPW - 1;
-  const f32x16 s0 = sum4(ja);
-  const f32x16 s1 = (DUAL || NPW == 2) ? sum4(jb) : s0;
-  const int m = l32;
-  if (m >= rows) return;
-  if constexpr (SPLITTABLE) {
-    if (split_slot >= 0) {
-      // raw fp32 partial sums, tile-local rows x 256 columns (SwiGLU: gate
-      // sums in [0,128), up sums in [128,256)), as the other tiles store them
-      float* dst = a.partial + (int64_t)split_slot * a.split_rows * kSplitTileCols + m * kSplitTileCols;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int c = 8 * q4 + 4 * h;
-        *reinterpret_cast<float4*>(dst + ja * kStrip + c) =
-            float4{s0[4 * q4], s0[4 * q4 + 1], s0[4 * q4 + 2], s0[4 * q4 + 3]};
-        *reinterpret_cast<float4*>(dst + jb * kStrip + c) =
-            float4{s1[4 * q4], s1[4 * q4 + 1], s1[4 * q4 + 2], s1[4 * q4 + 3]};
-      }
-      return;
-    }
-  }
+  // Output units (half, strips) each wave finishes.  SwiGLU: the gate and up
+  // strips of h columns 32i .. 32i+31 (strips i and i + NS/2); otherwise one
+  // strip.  RH = 1: SwiGLU i = w (NS = 4: waves 0 and 1 only), otherwise
+  // strips 2w and 2w+1 (NS = 8) or strip w (NS = 4).  RH = 2 (NS = 4):
+  // SwiGLU i = w & 1 of half w >> 1; otherwise strip w of both halves.
+  constexpr int NPW = DUAL ? 1 : (RH == 2 ? 2 : NS / 4);  // output units per wave
+  if (RH == 1 && DUAL && w >= NS / 2) return;
   const float* bias = a.bias ? a.bias + (int64_t)e * a.bias_estride : nullptr;
-  const RowCtx rc = row_ctx<EPI>(a, r0 + m);
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    const f32x4 v0{s0[4 * q4], s0[4 * q4 + 1], s0[4 * q4 + 2], s0[4 * q4 + 3]};
-    const f32x4 v1{s1[4 * q4], s1[4 * q4 + 1], s1[4 * q4 + 2], s1[4 * q4 + 3]};
-    if constexpr (DUAL) {
-      epilogue4<elem, EPI>(a, rc, n0 + ja * kStrip + 8 * q4 + 4 * h, v0, v1, bias);
+  for (int u = 0; u < NPW; ++u) {
+    int hh, ja, jb;
+    if constexpr (RH == 2) {
+      hh = DUAL ? (w >> 1) : u;
+      ja = DUAL ? (w & 1) : w;
+      jb = DUAL ? ja + NS / 2 : ja;
     } else {
-      epilogue4<elem, EPI>(a, rc, n0 + ja * kStrip + 8 * q4 + 4 * h, v0, v0, bias);
-      if constexpr (NPW == 2) epilogue4<elem, EPI>(a, rc, n0 + jb * kStrip + 8 * q4 + 4 * h, v1, v1, bias);
+      hh = 0;
+      ja = DUAL ? w : NPW * w + u;
+      jb = DUAL ? w + NS / 2 : ja;
+    }
+    const f32x16 s0 = sum4(hh, ja);
+    const f32x16 s1 = DUAL ? sum4(hh, jb) : s0;
+    const int m = 32 * hh + l32;
+    if (m >= rows) continue;
+    if constexpr (SPLITTABLE) {
+      if (split_slot >= 0) {
+        // raw fp32 partial sums, tile-local rows x 256 columns (SwiGLU: gate
+        // sums in [0,128), up sums in [128,256)), as the other tiles store them
+        float* dst = a.partial + (int64_t)split_slot * a.split_rows * kSplitTileCols + m * kSplitTileCols;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int c = 8 * q4 + 4 * h;
+          *reinterpret_cast<float4*>(dst + ja * kStrip + c) =
+              float4{s0[4 * q4], s0[4 * q4 + 1], s0[4 * q4 + 2], s0[4 * q4 + 3]};
+          if constexpr (DUAL)
+            *reinterpret_cast<float4*>(dst + jb * kStrip + c) =
+                float4{s1[4 * q4], s1[4 * q4 + 1], s1[4 * q4 + 2], s1[4 * q4 + 3]};
+        }
+        continue;
+      }
+    }
+    const RowCtx rc = row_ctx<EPI>(a, r0 + m);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 v0{s0[4 * q4], s0[4 * q4 + 1], s0[4 * q4 + 2], s0[4 * q4 + 3]};
+      const f32x4 v1{s1[4 * q4], s1[4 * q4 + 1], s1[4 * q4 + 2], s1[4 * q4 + 3]};
+      epilogue4<elem, EPI>(a, rc, n0 + ja * kStrip + 8 * q4 + 4 * h, v0, DUAL ? v1 : v0, bias);
     }
   }
 }
 
-template <int NS>
+template <int NS, int RH>
 hipError_t launch_ns(int epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
     case EPI_SWIGLU:
-      hipLaunchKernelGGL((gemm_stream_kernel<EPI_SWIGLU, NS>), dim3(a.max_work), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_stream_kernel<EPI_SWIGLU, NS, RH>), dim3(a.max_work), dim3(256), 0, s, a);
       break;
     case EPI_RELU:
-      hipLaunchKernelGGL((gemm_stream_kernel<EPI_RELU, NS>), dim3(a.max_work), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_stream_kernel<EPI_RELU, NS, RH>), dim3(a.max_work), dim3(256), 0, s, a);
       break;
     case EPI_DOWN_ATOMIC:
-      hipLaunchKernelGGL((gemm_stream_kernel<EPI_DOWN_ATOMIC, NS>), dim3(a.max_work), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_stream_kernel<EPI_DOWN_ATOMIC, NS, RH>), dim3(a.max_work), dim3(256), 0, s, a);
       break;
     default:
-      hipLaunchKernelGGL((gemm_stream_kernel<EPI_DOWN_SLOT, NS>), dim3(a.max_work), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_stream_kernel<EPI_DOWN_SLOT, NS, RH>), dim3(a.max_work), dim3(256), 0, s, a);
       break;
   }
   return hipGetLastError();
@@ -358,9 +386,10 @@ hipError_t launch_ns(int epi, const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gemm_stream(int epi, int strips, const GemmArgs& a, hipStream_t s) {
-  if (strips == 8) return launch_ns<8>(epi, a, s);
-  if (strips == 4) return launch_ns<4>(epi, a, s);
+hipError_t launch_gemm_stream(int epi, int strips, int rows, const GemmArgs& a, hipStream_t s) {
+  if (strips == 8 && rows == 32) return launch_ns<8, 1>(epi, a, s);
+  if (strips == 4 && rows == 32) return launch_ns<4, 1>(epi, a, s);
+  if (strips == 4 && rows == 64) return launch_ns<4, 2>(epi, a, s);
   return hipErrorInvalidValue;
 }
 

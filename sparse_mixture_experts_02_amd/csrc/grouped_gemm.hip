@@ -272,6 +272,7 @@ int variant_rows(int var) {
     case VAR_BF16_M32:
     case VAR_BF16_S32:
     case VAR_BF16_S32N: return 32;
+    case VAR_BF16_S64N: return 64;
     case VAR_GENERIC_M64: return 64;
     default: return 128;
   }
@@ -279,15 +280,16 @@ int variant_rows(int var) {
 
 int variant_cols(int var, bool dual) {
   if (var == VAR_GENERIC || var == VAR_GENERIC_M64) return 128;
-  if (var == VAR_BF16_S32N) return dual ? 64 : 128;
+  if (var == VAR_BF16_S32N || var == VAR_BF16_S64N) return dual ? 64 : 128;
   return dual ? 128 : 256;
 }
 
 hipError_t launch_grouped_gemm(int dtype, int epi, int var, const GemmArgs& a, hipStream_t s) {
   if (a.max_work <= 0 || a.N <= 0) return hipSuccess;
   if (var == VAR_GENERIC_M64) return dtype == 1 ? launch_tag<BF16, 64>(epi, a, s) : launch_tag<F32, 64>(epi, a, s);
-  if (var == VAR_BF16_S32 || var == VAR_BF16_S32N)
-    return dtype == 1 ? launch_gemm_stream(epi, var == VAR_BF16_S32 ? 8 : 4, a, s) : hipErrorInvalidValue;
+  if (var == VAR_BF16_S32 || var == VAR_BF16_S32N || var == VAR_BF16_S64N)
+    return dtype == 1 ? launch_gemm_stream(epi, var == VAR_BF16_S32 ? 8 : 4, var == VAR_BF16_S64N ? 64 : 32, a, s)
+                      : hipErrorInvalidValue;
   if (var != VAR_GENERIC) return launch_gemm_bf16(dtype, epi, var, a, s);
   return dtype == 1 ? launch_tag<BF16, 128>(epi, a, s) : launch_tag<F32, 128>(epi, a, s);
 }

@@ -169,6 +169,7 @@ enum Variant {
   VAR_GENERIC_M64 = 4,
   VAR_BF16_S32 = 5,   // weight-streaming 32-row tiles of 256 weight rows (gemm_stream.hip)
   VAR_BF16_S32N = 6,  // the same with 128 weight rows per tile, never split along K
+  VAR_BF16_S64N = 7,  // the narrow streaming tile over 64 sorted rows (two 32-row halves)
 };
 int variant_rows(int var);
 int variant_cols(int var, bool dual);
@@ -216,7 +217,7 @@ hipError_t launch_gemm_bf16(int dtype, int epi, int var, const GemmArgs& a, hipS
 // The weight-streaming variants (bf16 only): `strips` = 8 (VAR_BF16_S32) or
 // 4 (VAR_BF16_S32N) strips of 32 weight rows per tile.
 constexpr int kStreamChunk = 512;  // K elements per chunk of the weight-streaming kernel
-hipError_t launch_gemm_stream(int epi, int strips, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_stream(int epi, int strips, int rows, const GemmArgs& a, hipStream_t s);
 
 struct FinalizeArgs {
   const float* src;   // slot rows (T*K, D) when K > 0 slots, or (T, D) accumulation

@@ -236,6 +236,11 @@ def test_noalloc_refuses_oversize_before_any_launch(lib):
     # (deterministic mode only; the atomic combine never splits)
     (dict(T=1, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=1), "stream_m32_narrow", "stream_m32"),
     (dict(T=1, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=0), "stream_m32_narrow", "stream_m32_narrow"),
+    # 128 and 200 tokens: 32 and 50 rows per expert -> the 64-row narrow streaming tile, which
+    # reads each expert's weights once for up to 64 rows; 100 tokens (25 rows) keeps 32-row tiles
+    (dict(T=128, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=1), "stream_m64_narrow", "stream_m64_narrow"),
+    (dict(T=200, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=0), "stream_m64_narrow", "stream_m64_narrow"),
+    (dict(T=100, D=4096, F=14336, E=8, K=2, dtype=1, deterministic=1), "stream_m32_narrow", "stream_m32_narrow"),
     # the same in fp32: the direct 32-row tiles
     (dict(T=64, D=4096, F=14336, E=8, K=2, dtype=0), "direct_m32", "direct_m32"),
     # gate_up contracts over D = 768 (not a multiple of 512), down over F = 1024

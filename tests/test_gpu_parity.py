@@ -145,15 +145,21 @@ EDGE_LAST = [
 # its two-chunk loop), the narrow (128 weight rows) and wide (256, with its
 # last round split along K: parts of one and two chunks) tiles, the ReLU and
 # SwiGLU epilogues, a column tail off the tile width, experts with more than
-# 32 rows.  The last field names the kernels the plan must pick (gate_up,
-# down) in the atomic and in the deterministic mode.
-S, SN, M32, G64 = "stream_m32", "stream_m32_narrow", "direct_m32", "generic_m64"
+# 32 rows, and the 64-row narrow tile (28 or more rows per expert on
+# average: one or two 32-row halves, experts with more than 64 rows over
+# several tiles under the Zipf bias).  The last field names the kernels the
+# plan must pick (gate_up, down) in the atomic and in the deterministic mode.
+S, SN, S64, M32, G64 = "stream_m32", "stream_m32_narrow", "stream_m64_narrow", "direct_m32", "generic_m64"
 STREAM = [
     (40, 1024, 1536, 8, 2, "swiglu", "bf16", False, True, {False: (SN, SN), True: (SN, SN)}),
     (24, 1536, 2048, 4, 2, "relu", "bf16", True, True, {False: (SN, SN), True: (SN, SN)}),
     (16, 8192, 512, 4, 2, "swiglu", "bf16", False, True, {False: (S, SN), True: (S, SN)}),
     (30, 512, 1056, 8, 2, "swiglu", "bf16", True, False, {False: (SN, G64), True: (SN, G64)}),
     (50, 2560, 512, 8, 3, "relu", "bf16", False, True, {False: (SN, SN), True: (SN, SN)}),
+    (128, 1024, 1536, 8, 2, "swiglu", "bf16", False, True, {False: (S64, S64), True: (S64, S64)}),
+    (200, 1024, 1536, 8, 2, "swiglu", "bf16", False, False, {False: (S64, S64), True: (S64, S64)}),
+    (100, 1536, 2048, 4, 2, "relu", "bf16", True, True, {False: (S64, S64), True: (S64, S64)}),
+    (120, 512, 1056, 8, 2, "swiglu", "bf16", True, True, {False: (S64, G64), True: (S64, G64)}),
     (3, 512, 4096, 4, 2, "relu", "bf16", True, True, {False: (SN, SN), True: (SN, S)}),
 ]
 
