@@ -128,7 +128,7 @@ moe_status moe_forward(const moe_desc* d, const void* x, const void* router, con
  * (and of the same atomic adds with 0).  MOE_EDEVICE if the array's device
  * address cannot be obtained.
  */
-#define MOE_NOALLOC_MAX_BYTES (64u << 20)
+#define MOE_NOALLOC_MAX_BYTES (128u << 20)
 moe_status moe_forward_noalloc(const moe_desc* d, const void* x, const void* router, const void* gate_up_proj,
                                const void* down_proj, const float* router_bias, const float* up_bias,
                                const float* down_bias, void* out, int64_t* selected_experts,

@@ -131,7 +131,7 @@ def moe_probe_read(buf, nbytes, blocks, out, stream) -> int:
     return load_library().moe_probe_read(buf, int(nbytes), int(blocks), out, stream)
 
 
-GEMM_VARIANTS = {0: "generic_m128", 1: "direct_m256_tail", 2: "direct_m128", 3: "direct_m32", 4: "generic_m64",
+GEMM_VARIANTS = {0: "generic_m128", 1: "direct_m256_tail", 3: "direct_m32", 4: "generic_m64",
                  5: "stream_m32", 6: "stream_m32_narrow", 7: "stream_m64_narrow"}
 
 
@@ -165,7 +165,7 @@ def moe_forward(desc, x, router, gate_up_proj, down_proj, router_bias, up_bias, 
                                       expert_counts, workspace, workspace_bytes, stream)
 
 
-MOE_NOALLOC_MAX_BYTES = 64 << 20
+MOE_NOALLOC_MAX_BYTES = 128 << 20
 
 
 def moe_forward_noalloc(desc, x, router, gate_up_proj, down_proj, router_bias, up_bias, down_bias, out,

@@ -12,8 +12,10 @@
 // columns of one row.
 // The 256-row tile runs 8 waves (two per SIMD) as a 4 x 2 grid of 64 x 128
 // wave tiles and can take an expert's tail of up to kTailRows more rows; the
-// 128-row tile runs 4 waves (2 x 2); the decode tile (BM 32) runs 4 waves
-// side by side along the weight rows.
+// decode tile (BM 32) runs 4 waves side by side along the weight rows.  (A
+// 4-wave 128-row tile for 64-511 rows per expert measured 17-35% slower than
+// the 256-row tile on bf16 layers and up to 3.3x slower on fp32 ones, whose
+// partial last round it could not split along K; removed.)
 //
 // Data path: global_load_lds_dwordx4 writes each 16-byte chunk straight from
 // HBM/L2 into LDS (no staging registers).  LDS holds S stages of KB bytes of
@@ -92,7 +94,6 @@ struct Shape {
 // (which need twice the barriers); the decode tile is a weight stream and
 // wants more bytes in flight.
 using ShapeM256 = Shape<256, 8, 4, 128, 2>;  // 2 x 68 KB of LDS (with the tail rows)
-using ShapeM128 = Shape<128, 4, 2, 128, 2>;  // 2 x 48 KB
 using ShapeM32 = Shape<32, 4, 1, 128, 4>;    // 4 x 36 KB
 
 // SHORT_K: the instance of the bf16 256-row tile for short contractions (at
@@ -730,9 +731,6 @@ hipError_t launch_rows(int var, const GemmArgs& a, hipStream_t s) {
         }
       }
       hipLaunchKernelGGL((gemm_bf16_kernel<T, EPI, ShapeM256>), dim3(a.max_work), dim3(ShapeM256::NW * 64), 0, s, a);
-      break;
-    case VAR_BF16_M128:
-      hipLaunchKernelGGL((gemm_bf16_kernel<T, EPI, ShapeM128>), dim3(a.max_work), dim3(ShapeM128::NW * 64), 0, s, a);
       break;
     default:
       hipLaunchKernelGGL((gemm_bf16_kernel<T, EPI, ShapeM32>), dim3(a.max_work), dim3(ShapeM32::NW * 64), 0, s, a);

@@ -125,7 +125,7 @@ struct WorkSpec {
   int2* split_tiles;   // (split_ncu)
   int32_t* split_info; // (2): R, P
   // Order in which the XCDs take the items: 1, 32-item windows dealt out in
-  // turn (the 256- and 128-row tiles, whose rounds then share operands in
+  // turn (the 256-row tiles, whose rounds then share operands in
   // L2); 0, one contiguous range per XCD (the 32-row decode tile, a weight
   // stream, and the generic kernel).
   int32_t windows;
@@ -159,12 +159,12 @@ enum Epilogue { EPI_SWIGLU = 0, EPI_RELU = 1, EPI_DOWN_ATOMIC = 2, EPI_DOWN_SLOT
 //            for GEMMs with too few 128-row items to fill two rounds).
 //   BF16_Mxxx: bf16 with K a multiple of 64, or fp32 with K a multiple of 32
 //            (whole 128-byte stages), 16-byte aligned rows; LDS stages filled
-//            by direct global->LDS loads; xxx rows per tile (256 and 128 for
-//            prefill, 32 for decode-sized segments).
+//            by direct global->LDS loads; xxx rows per tile (256 from 64
+//            rows per expert on, 32 for decode-sized segments).  Value 2 is
+//            retired (a 128-row tile, slower than the 256-row one).
 enum Variant {
   VAR_GENERIC = 0,
   VAR_BF16_M256 = 1,
-  VAR_BF16_M128 = 2,
   VAR_BF16_M32 = 3,
   VAR_GENERIC_M64 = 4,
   VAR_BF16_S32 = 5,   // weight-streaming 32-row tiles of 256 weight rows (gemm_stream.hip)

@@ -109,6 +109,9 @@ EDGE = [
     # ragged row tiles and column tails: 128-row, 256-row and 32-row tiles
     (1000, 128, 320, 4, 2, "swiglu", "bf16", False, True),
     (600, 192, 448, 3, 1, "relu", "bf16", True, True),
+    # fp32 between 64 and 512 rows per expert (256-row tiles, mostly partial)
+    (1000, 128, 320, 4, 2, "swiglu", "f32", False, True),
+    (600, 192, 448, 3, 1, "relu", "f32", True, True),
     (4096, 128, 192, 4, 2, "swiglu", "bf16", False, True),
     # 256-row tiles whose columns all lie inside N, without biases: the
     # interior-tile epilogue of the ReLU and down tiles

@@ -56,7 +56,7 @@ def _run(inp, d, noalloc):
 
 CALLS = [
     # (T, D, F, E, K, act, dtype, biases): the second call is smaller than the first
-    (1000, 256, 512, 8, 2, "swiglu", "bf16", False),   # 128-row tiles
+    (1000, 256, 512, 8, 2, "swiglu", "bf16", False),   # 256-row tiles with K-split parts (76 MiB)
     (40, 512, 768, 8, 2, "swiglu", "bf16", False),     # 32-row tiles with K-split parts
 ]
 
