@@ -1,11 +1,11 @@
-// Weight-streaming grouped GEMM for decode-sized expert segments (bf16, at
-// most 32 rows per expert tile): the gate_up and down projections when each
+// Weight-streaming grouped GEMM for decode-sized expert segments (bf16, 32
+// or 64 rows per expert tile): the gate_up and down projections when each
 // expert holds only a few tokens, so the product is bound by reading the
 // active experts' weights once from HBM (the Dew "Mixture of experts" page,
 // section "Expert computation and placement": the sorted rows of each expert
 // run as one grouped product; epilogues as in gemm_epilogue.h).
 //
-// Tile: up to 32 sorted rows x 32*NS weight rows, NS = 8 or 4 strips of 32
+// Tile: up to 32 (or, narrow, 64) sorted rows x 32*NS weight rows, NS = 8 or 4 strips of 32
 // (SwiGLU: NS/2 gate strips and the matching up strips -> 16*NS h columns).
 // The wide tile (NS = 8) has the shape of gemm_bf16.hip's 32-row tile, with
 // its work lists and K split; the narrow one (NS = 4) has twice the column
