@@ -449,6 +449,27 @@ def test_decode_mixtral_shape_full():
 
 
 @pytest.mark.slow
+def test_decode_128_tokens_full_size_64_row_tiles():
+    """The first 128 prefill tokens at the real Mixtral shape: 32 rows per
+    expert on average, so both GEMMs run the 64-row weight-streaming tiles
+    (each expert's weights read once); every token compared."""
+    base = _prefill_family()
+    c = base["cfg"]
+    T = 128
+    inp = dict(base, cfg=dict(c, T=T), x=base["x"][:T])
+    d = _CACHE.get("prefill_dev") or device_inputs(base)
+    dd = dict(d, x=d["x"][:T].contiguous())
+    desc = moe.make_desc(T, c["D"], c["F"], c["E"], c["K"], dtype=torch.bfloat16, deterministic=True)
+    plan = moe.moe_gemm_plan(desc)
+    assert plan["gate_up"]["variant"] == plan["down"]["variant"] == "stream_m64_narrow", plan
+    _say("decode T=128 D=4096 F=14336 E=8 K=2 bf16 (64-row streaming tiles)")
+    g = gpu_forward(inp, dd)
+    assert int(g["counts"].max()) > 32  # some expert holds both halves of a tile
+    check_full_properties(inp, g)
+    _say(str(check(inp, g)))
+
+
+@pytest.mark.slow
 def test_one_expert_share_full_size():
     """One GPU's share under expert sharding: E = K = 1 at the Mixtral D and F
     (every token goes to the one expert, whose weight p/(p+1e-9) is 1 in
