@@ -81,13 +81,16 @@ GemmPlan plan_gemm(const moe_desc* d, int64_t M, int64_t N, int64_t Kd, int64_t 
                          b_expert_elems * eb < (int64_t)UINT32_MAX;
   if (direct_ok) {
     const int64_t mean = M / d->E;
-    // The 8-wave ping-pong 256-row tile from 64 rows per expert on, even
+    // The 8-wave ping-pong 256-row tile from 58 rows per expert on, even
     // where most of its rows are empty (the idle waves skip their MFMAs): on
     // the Mixtral-shaped layer at 256-1536 tokens (64-384 rows per expert) it
     // runs the layer 17-35% faster than the 4-wave 128-row tile it replaced,
     // on fp32 ReLU layers with 32-256 rows per expert 1.8-3.3x faster (that
-    // tile could not split its partial last round along K).
-    p.var = mean >= 64 ? VAR_BF16_M256 : VAR_BF16_M32;
+    // tile could not split its partial last round along K).  Below it, the
+    // 64-row streaming tile (bf16) wins up to about 55 rows per expert (180-
+    // 220 tokens: 0.50-0.52 against 0.65 ms) and loses from about 60 (240
+    // tokens: 0.728 against 0.656 ms, once experts pass 64 rows).
+    p.var = mean >= 58 ? VAR_BF16_M256 : VAR_BF16_M32;
     // Decode-sized bf16 segments: the weight-streaming kernel, which reads
     // every weight row in 1 KB runs.  Its wide tiles (256 weight rows) have
     // their last partial round split along K, which costs a fix-up launch;

@@ -250,10 +250,13 @@ def test_noalloc_refuses_oversize_before_any_launch(lib):
     (dict(T=64, D=1024, F=1040, E=8, K=2, dtype=1), "direct_m32", "generic_m64"),
     # the 128-expert layer: 1024 rows per expert -> 256-row tiles
     (dict(T=16384, D=2048, F=768, E=128, K=8, dtype=1), "direct_m256_tail", "direct_m256_tail"),
-    # bf16 from 64 rows per expert: the 256-row ping-pong tile (250 rows per expert here)
+    # bf16 from 58 rows per expert: the 256-row ping-pong tile (250 rows per expert here; 60 and
+    # 64 at 240 and 256 tokens, where 220 tokens, 55 rows, still streams on 64-row tiles)
     (dict(T=1000, D=512, F=1024, E=8, K=2, dtype=1), "direct_m256_tail", "direct_m256_tail"),
     (dict(T=256, D=4096, F=14336, E=8, K=2, dtype=1), "direct_m256_tail", "direct_m256_tail"),
-    # fp32 too: 256-row tiles from 64 rows per expert
+    (dict(T=240, D=4096, F=14336, E=8, K=2, dtype=1), "direct_m256_tail", "direct_m256_tail"),
+    (dict(T=220, D=4096, F=14336, E=8, K=2, dtype=1), "stream_m64_narrow", "stream_m64_narrow"),
+    # fp32 too: 256-row tiles from 58 rows per expert
     (dict(T=1000, D=512, F=1024, E=8, K=2, dtype=0), "direct_m256_tail", "direct_m256_tail"),
     # K not filling 128-byte stages -> the generic kernel
     (dict(T=1000, D=40, F=48, E=8, K=2, dtype=0), "generic_m64", "generic_m64"),
