@@ -150,9 +150,12 @@ EDGE_LAST = [
 # SwiGLU epilogues, a column tail off the tile width, experts with more than
 # 32 rows, and the 64-row narrow tile (28 or more rows per expert on
 # average: one or two 32-row halves, experts with more than 64 rows over
-# several tiles under the Zipf bias).  The last field names the kernels the
-# plan must pick (gate_up, down) in the atomic and in the deterministic mode.
+# several tiles under the Zipf bias), and both sides of the switch to the
+# 256-row tile at 58 rows per expert on average (228 and 232 tokens).  The
+# last field names the kernels the plan must pick (gate_up, down) in the
+# atomic and in the deterministic mode.
 S, SN, S64, M32, G64 = "stream_m32", "stream_m32_narrow", "stream_m64_narrow", "direct_m32", "generic_m64"
+M256 = "direct_m256_tail"
 STREAM = [
     (40, 1024, 1536, 8, 2, "swiglu", "bf16", False, True, {False: (SN, SN), True: (SN, SN)}),
     (24, 1536, 2048, 4, 2, "relu", "bf16", True, True, {False: (SN, SN), True: (SN, SN)}),
@@ -163,6 +166,8 @@ STREAM = [
     (200, 1024, 1536, 8, 2, "swiglu", "bf16", False, False, {False: (S64, S64), True: (S64, S64)}),
     (100, 1536, 2048, 4, 2, "relu", "bf16", True, True, {False: (S64, S64), True: (S64, S64)}),
     (120, 512, 1056, 8, 2, "swiglu", "bf16", True, True, {False: (S64, G64), True: (S64, G64)}),
+    (228, 1024, 1536, 8, 2, "swiglu", "bf16", False, True, {False: (S64, S64), True: (S64, S64)}),
+    (232, 1024, 1536, 8, 2, "swiglu", "bf16", True, True, {False: (M256, M256), True: (M256, M256)}),
     (3, 512, 4096, 4, 2, "relu", "bf16", True, True, {False: (SN, SN), True: (SN, S)}),
 ]
 
